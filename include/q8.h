@@ -1,0 +1,153 @@
+/*
+ * q8.h -- C ABI of libq8proj.so, the MI355X (gfx950) Q8_0 projection library.
+ *
+ * The projection is the wide product that a compiled decode step, a batched
+ * decode step and a prefill chunk spend their bytes on: a matrix of Q8_0
+ * weights times a stack of activation rows, every weight read once for the
+ * whole stack (logicaffeine_compile, codegen_cuda::lane page, description;
+ * model::author page, Functions: prefill, decode_batch).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All pointers are caller-owned device memory (the weight array may also be
+ *    host memory the device maps: a kernel reads it through the same pointer and
+ *    the result does not change; codegen_cuda::lane page, Modules: residence).
+ *    The library allocates, frees and synchronizes nothing, and never reads
+ *    device memory on the host (codegen_cuda::lane page, Modules: arena), so
+ *    every call may be captured into a HIP graph.
+ *  - `stream` is a hipStream_t (NULL: the null stream).  Work is enqueued
+ *    asynchronously; results are ready when the stream is.
+ *  - Arguments are validated before anything is enqueued; a failed check
+ *    returns its named status and enqueues nothing (errors by name, as the
+ *    lane's LaneError reports why a step does not compile; codegen_cuda::lane
+ *    page, Enums: LaneError).  An empty problem (n == 0 or rows == 0) returns
+ *    Q8_OK and enqueues nothing.  A launch failure returns Q8_E_HIP.  Device
+ *    faults surface at the caller's next synchronization.
+ *  - Inputs must be finite; NaN or infinity gives unspecified outputs.
+ *
+ * Data layout
+ * -----------
+ *  - Q8_0 weights W (n x k, out x in) are stored as in a checkpoint, read in
+ *    place (codegen_cuda::lane page, description; model::author page,
+ *    description: Q8_0 quants and block scales; spatial::streamed page,
+ *    description: a weight is consumed as it is stored).  Row-major
+ *    [n][k/32] blocks of 34 bytes: the block's binary16 scale d (little-endian),
+ *    then 32 int8 values q.  Row n starts at byte n * (k/32) * 34.  The weight
+ *    value is d * q.
+ *  - Activation stacks are row-major [rows][k].  Quantized activations are
+ *    hi and (two-word only) lo int8 [rows][k] and f32 block scales
+ *    scale [rows][k/32].  Outputs and residuals are row-major f32 [rows][n].
+ *  - k must be a positive multiple of 64 (whole blocks, dword-aligned rows).
+ *
+ * Numerics (codegen_cuda::lane page, description: the `activations` knob)
+ * ----------------------------------------------------------------------
+ *  Q8_ACT_F32  : f32 activations x; every product and sum in f64, rounded once
+ *                to f32:  y = sum_b d_b * sum_j q_j * x_j  (+ residual).
+ *  Q8_ACT_I8   : one int8 word per value (llama.cpp's block form): per
+ *                32-column block s = max|x|/127 (f32), hi = rha(x/s).
+ *                y = sum_b d_b * s_b * S_hi_b, S_hi_b = sum_j q_j * hi_j (int32).
+ *  Q8_ACT_I8X2 : two words, ~14 bits (the lane's default): as one-word plus
+ *                lo = rha((fma(-s, hi, x) * 128) / s) on the same scale.
+ *                y = sum_b d_b * s_b * (S_hi_b + S_lo_b / 128).
+ *  rha is round-half-away-from-zero, divisions are correctly rounded f32, an
+ *  all-zero block gives zero quants.  The integer block sums are exact; the
+ *  block terms are accumulated in f64 and each output is rounded once to f32.
+ */
+#ifndef Q8PROJ_Q8_H
+#define Q8PROJ_Q8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Activation numerics (the lane's `activations` knob). */
+typedef enum {
+    Q8_ACT_F32 = 0,  /* f32 activations, f64 sums */
+    Q8_ACT_I8 = 1,   /* one int8 word */
+    Q8_ACT_I8X2 = 2  /* two int8 words, the default */
+} q8_act_mode;
+
+/* Named results. */
+typedef enum {
+    Q8_OK = 0,
+    Q8_E_NULL = 1,   /* a required pointer is NULL */
+    Q8_E_SHAPE = 2,  /* negative size, k not a positive multiple of 64, or a size too large */
+    Q8_E_ALIGN = 3,  /* a pointer breaks the alignment its argument requires */
+    Q8_E_MODE = 4,   /* unknown mode, or a mode this entry point does not take */
+    Q8_E_ALIAS = 5,  /* an output overlaps an input (other than y == residual exactly) */
+    Q8_E_HIP = 6     /* the HIP runtime refused a launch */
+} q8_status;
+
+/* Q8_0-quantize an f32 weight matrix (off the projection's path: a checkpoint
+ * already stores Q8_0; model::author page, description).  Per 32-block:
+ * d = binary16(max|w| / 127) (round to nearest even), q = clamp(rha(w / d),
+ * -127, 127) dividing by the stored binary16 value, q = 0 when d == 0.
+ *   w      : f32 [n][k], 4-byte aligned.
+ *   blocks : out, n * (k/32) * 34 bytes, 4-byte aligned, must not overlap w.
+ * Errors: Q8_E_NULL, Q8_E_SHAPE, Q8_E_ALIGN, Q8_E_ALIAS, Q8_E_HIP. */
+q8_status q8_quantize_weights(const float *w, int64_t n, int64_t k, void *blocks, void *stream);
+
+/* Quantize an activation stack for the integer modes (codegen_cuda::lane page,
+ * description: the one-word and two-word activations; Modules, kernels: an
+ * activation quantized for its projection).
+ *   mode   : Q8_ACT_I8 or Q8_ACT_I8X2 (Q8_ACT_F32 needs no quantization:
+ *            Q8_E_MODE).
+ *   x      : f32 [rows][k], 16-byte aligned.
+ *   hi, lo : out, int8 [rows][k], 16-byte aligned; lo is required for
+ *            Q8_ACT_I8X2 and ignored (may be NULL) for Q8_ACT_I8.
+ *   scale  : out, f32 [rows][k/32], 4-byte aligned.
+ * Outputs must not overlap x or each other.
+ * Errors: Q8_E_NULL, Q8_E_SHAPE, Q8_E_ALIGN, Q8_E_MODE, Q8_E_ALIAS, Q8_E_HIP. */
+q8_status q8_quantize_act(int mode, const float *x, int64_t rows, int64_t k, int8_t *hi, int8_t *lo,
+                          float *scale, void *stream);
+
+/* y = W x (+ residual) for ONE activation row: the decode step's projection
+ * (codegen_cuda::lane page, description: projections read in place).
+ *   mode        : q8_act_mode.
+ *   w           : Q8_0 blocks of an n x k matrix, 4-byte aligned (device or
+ *                 host-mapped memory).
+ *   hi, lo, scale : the row quantized by q8_quantize_act (integer modes;
+ *                 hi/lo 16-byte aligned, lo only for Q8_ACT_I8X2); NULL in
+ *                 Q8_ACT_F32.
+ *   x           : f32 [k], 16-byte aligned, Q8_ACT_F32 only (NULL otherwise).
+ *   residual    : f32 [n] added to the result, or NULL.  4-byte aligned.
+ *   y           : out, f32 [n], 4-byte aligned.  May be exactly `residual`
+ *                 (in-place add); must not otherwise overlap any input.
+ * Errors: Q8_E_NULL, Q8_E_SHAPE, Q8_E_ALIGN, Q8_E_MODE, Q8_E_ALIAS, Q8_E_HIP. */
+q8_status q8_matvec(int mode, const void *w, int64_t n, int64_t k, const int8_t *hi, const int8_t *lo,
+                    const float *scale, const float *x, const float *residual, float *y, void *stream);
+
+/* Y = X W^T (+ residual) for a stack of `rows` activation rows, every weight
+ * block read once per stack of up to 64 rows: a batched decode step (one row a
+ * sequence) or a prefill chunk (model::author page, Functions: decode_batch,
+ * prefill; codegen_cuda::lane page, description: chunks of 2, 4, ... rows).
+ * Arguments as q8_matvec with [rows][...] stacks: hi/lo/x [rows][k],
+ * scale [rows][k/32], residual and y [rows][n].  rows >= 1; stacks wider than
+ * 64 rows are run as consecutive 64-row slices.
+ * Errors: Q8_E_NULL, Q8_E_SHAPE, Q8_E_ALIGN, Q8_E_MODE, Q8_E_ALIAS, Q8_E_HIP. */
+q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
+                         const int8_t *lo, const float *scale, const float *x, const float *residual,
+                         float *y, void *stream);
+
+/* The exact int32 block dot products of the integer modes, for checking:
+ *   sums[r][n][b][0] = sum_j q[n][b][j] * hi[r][32b+j]
+ *   sums[r][n][b][1] = sum_j q[n][b][j] * lo[r][32b+j]   (Q8_ACT_I8X2 only)
+ * computed with the same device block decode and dot routine as the
+ * projection kernels of rows <= 8.  sums: out, int32 [rows][n][k/32][words],
+ * 4-byte aligned.  Errors as q8_matmul_rows (Q8_ACT_F32: Q8_E_MODE). */
+q8_status q8_block_sums(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
+                        const int8_t *lo, int32_t *sums, void *stream);
+
+/* Name of a status ("Q8_OK", "Q8_E_SHAPE", ...); "Q8_E_UNKNOWN" otherwise. */
+const char *q8_status_name(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int q8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8PROJ_Q8_H */

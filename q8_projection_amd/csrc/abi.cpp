@@ -1,0 +1,205 @@
+// abi.cpp -- the C ABI of libq8proj.so: argument validation, then dispatch to
+// the HIP launchers on the caller's stream.  Nothing here allocates, frees,
+// synchronizes or reads device memory (codegen_cuda::lane page, Modules: arena;
+// every call can be captured into a graph, as the lane captures each step).
+// Errors are named (codegen_cuda::lane page, Enums: LaneError) and returned
+// before anything is enqueued.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/q8.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxK = int64_t(1) << 24;           // columns
+constexpr int64_t kMaxBlocks = int64_t(1) << 27;      // n * k/32 (4.5 GB of weights)
+constexpr int64_t kMaxRowsTimesN = int64_t(1) << 31;  // elements of y
+constexpr int kMaxDevices = 64;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Do byte ranges [a, a+an) and [b, b+bn) overlap?
+bool overlap(const void *a, int64_t an, const void *b, int64_t bn) {
+    if (!a || !b || an <= 0 || bn <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + static_cast<uintptr_t>(bn) && b0 < a0 + static_cast<uintptr_t>(an);
+}
+
+q8_status check_k(int64_t k) {
+    if (k <= 0 || k % 64 != 0 || k > kMaxK) return Q8_E_SHAPE;
+    return Q8_OK;
+}
+
+q8_status from_hip(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_E_HIP; }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Validation shared by q8_matvec / q8_matmul_rows / q8_block_sums.
+q8_status check_projection(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
+                           const int8_t *lo, const float *scale, const float *x, const float *residual,
+                           const void *out, int64_t out_bytes, bool f32_allowed, bool need_scale) {
+    if (mode != Q8_ACT_F32 && mode != Q8_ACT_I8 && mode != Q8_ACT_I8X2) return Q8_E_MODE;
+    if (mode == Q8_ACT_F32 && !f32_allowed) return Q8_E_MODE;
+    if (n < 0 || rows < 0) return Q8_E_SHAPE;
+    if (q8_status s = check_k(k); s != Q8_OK) return s;
+    const int64_t nb = k / 32;
+    if (n > kMaxBlocks / nb || rows * n > kMaxRowsTimesN || rows > kMaxRowsTimesN / 64) return Q8_E_SHAPE;
+    if (!w || !out) return Q8_E_NULL;
+    if (mode == Q8_ACT_F32) {
+        if (!x) return Q8_E_NULL;
+    } else {
+        if (!hi || (need_scale && !scale)) return Q8_E_NULL;
+        if (mode == Q8_ACT_I8X2 && !lo) return Q8_E_NULL;
+    }
+    if (!aligned(w, 4) || !aligned(out, 4)) return Q8_E_ALIGN;
+    if (residual && !aligned(residual, 4)) return Q8_E_ALIGN;
+    if (mode == Q8_ACT_F32) {
+        if (!aligned(x, 16)) return Q8_E_ALIGN;
+    } else {
+        if (!aligned(hi, 16) || (need_scale && !aligned(scale, 4))) return Q8_E_ALIGN;
+        if (mode == Q8_ACT_I8X2 && !aligned(lo, 16)) return Q8_E_ALIGN;
+    }
+    const int64_t wbytes = n * nb * 34;
+    const int64_t abytes = rows * k;
+    if (overlap(out, out_bytes, w, wbytes)) return Q8_E_ALIAS;
+    if (mode == Q8_ACT_F32) {
+        if (overlap(out, out_bytes, x, abytes * 4)) return Q8_E_ALIAS;
+    } else {
+        if (overlap(out, out_bytes, hi, abytes)) return Q8_E_ALIAS;
+        if (need_scale && overlap(out, out_bytes, scale, rows * nb * 4)) return Q8_E_ALIAS;
+        if (mode == Q8_ACT_I8X2 && overlap(out, out_bytes, lo, abytes)) return Q8_E_ALIAS;
+    }
+    if (residual && residual != out && overlap(out, out_bytes, residual, rows * n * 4)) return Q8_E_ALIAS;
+    return Q8_OK;
+}
+
+}  // namespace
+
+namespace q8 {
+
+DeviceInfo device_info() {
+    static DeviceInfo cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+    DeviceInfo &c = cache[dev];
+    if (c.cus == 0) {
+        int cus = 0, lds = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || lds <= 0)
+            lds = 64 * 1024;
+        c.lds_per_block = lds;
+        c.cus = cus;
+    }
+    return c;
+}
+
+}  // namespace q8
+
+extern "C" {
+
+q8_status q8_quantize_weights(const float *w, int64_t n, int64_t k, void *blocks, void *stream) {
+    if (n < 0) return Q8_E_SHAPE;
+    if (q8_status s = check_k(k); s != Q8_OK) return s;
+    if (n > kMaxBlocks / (k / 32)) return Q8_E_SHAPE;
+    if (!w || !blocks) return Q8_E_NULL;
+    if (!aligned(w, 4) || !aligned(blocks, 4)) return Q8_E_ALIGN;
+    if (overlap(blocks, n * (k / 32) * 34, w, n * k * 4)) return Q8_E_ALIAS;
+    if (n == 0) return Q8_OK;
+    return from_hip(q8::launch_quantize_weights(w, n, k, static_cast<uint8_t *>(blocks), as_stream(stream)));
+}
+
+q8_status q8_quantize_act(int mode, const float *x, int64_t rows, int64_t k, int8_t *hi, int8_t *lo,
+                          float *scale, void *stream) {
+    if (mode != Q8_ACT_I8 && mode != Q8_ACT_I8X2) return Q8_E_MODE;
+    if (rows < 0) return Q8_E_SHAPE;
+    if (q8_status s = check_k(k); s != Q8_OK) return s;
+    if (rows > kMaxBlocks / (k / 32)) return Q8_E_SHAPE;
+    if (!x || !hi || !scale || (mode == Q8_ACT_I8X2 && !lo)) return Q8_E_NULL;
+    if (!aligned(x, 16) || !aligned(hi, 16) || !aligned(scale, 4) || (mode == Q8_ACT_I8X2 && !aligned(lo, 16)))
+        return Q8_E_ALIGN;
+    const int64_t nv = rows * k, nbk = rows * (k / 32);
+    if (overlap(hi, nv, x, nv * 4) || overlap(scale, nbk * 4, x, nv * 4) || overlap(hi, nv, scale, nbk * 4))
+        return Q8_E_ALIAS;
+    if (mode == Q8_ACT_I8X2 &&
+        (overlap(lo, nv, x, nv * 4) || overlap(lo, nv, hi, nv) || overlap(lo, nv, scale, nbk * 4)))
+        return Q8_E_ALIAS;
+    if (rows == 0) return Q8_OK;
+    return from_hip(q8::launch_quantize_act(mode == Q8_ACT_I8X2 ? 2 : 1, x, rows, k, hi,
+                                            mode == Q8_ACT_I8X2 ? lo : nullptr, scale, as_stream(stream)));
+}
+
+q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
+                         const int8_t *lo, const float *scale, const float *x, const float *residual,
+                         float *y, void *stream) {
+    if (q8_status s = check_projection(mode, w, n, k, rows, hi, lo, scale, x, residual, y, rows * n * 4, true, true);
+        s != Q8_OK)
+        return s;
+    if (n == 0 || rows == 0) return Q8_OK;
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const int64_t nb = k / 32;
+    const hipStream_t st = as_stream(stream);
+    // 64-row slices, each reading every weight block once.
+    for (int64_t r0 = 0; r0 < rows; r0 += 64) {
+        const int r = static_cast<int>(std::min<int64_t>(64, rows - r0));
+        const int8_t *shi = mode == Q8_ACT_F32 ? nullptr : hi + r0 * k;
+        const int8_t *slo = mode == Q8_ACT_I8X2 ? lo + r0 * k : nullptr;
+        const float *ssc = mode == Q8_ACT_F32 ? nullptr : scale + r0 * nb;
+        const float *sx = mode == Q8_ACT_F32 ? x + r0 * k : nullptr;
+        const float *sres = residual ? residual + r0 * n : nullptr;
+        float *sy = y + r0 * n;
+        hipError_t e;
+        if (r > 8 && q8::mfma_supports(mode, r)) {
+            e = q8::launch_mfma(mode, wb, n, k, r, shi, slo, ssc, sres, sy, st);
+        } else {
+            // the GEMV family, 8 rows at a time
+            e = hipSuccess;
+            for (int c0 = 0; c0 < r && e == hipSuccess; c0 += 8) {
+                const int c = std::min(8, r - c0);
+                e = q8::launch_gemv(mode, wb, n, k, c, shi ? shi + c0 * k : nullptr, slo ? slo + c0 * k : nullptr,
+                                    ssc ? ssc + c0 * nb : nullptr, sx ? sx + c0 * k : nullptr,
+                                    sres ? sres + c0 * n : nullptr, sy + c0 * n, st);
+            }
+        }
+        if (e != hipSuccess) return Q8_E_HIP;
+    }
+    return Q8_OK;
+}
+
+q8_status q8_matvec(int mode, const void *w, int64_t n, int64_t k, const int8_t *hi, const int8_t *lo,
+                    const float *scale, const float *x, const float *residual, float *y, void *stream) {
+    return q8_matmul_rows(mode, w, n, k, 1, hi, lo, scale, x, residual, y, stream);
+}
+
+q8_status q8_block_sums(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
+                        const int8_t *lo, int32_t *sums, void *stream) {
+    const int words = mode == Q8_ACT_I8X2 ? 2 : 1;
+    const int64_t out_bytes = (k > 0 && k % 64 == 0) ? rows * n * (k / 32) * words * 4 : 0;
+    if (q8_status s = check_projection(mode, w, n, k, rows, hi, lo, nullptr, nullptr, nullptr, sums, out_bytes,
+                                       false, false);
+        s != Q8_OK)
+        return s;
+    if (n == 0 || rows == 0) return Q8_OK;
+    return from_hip(q8::launch_block_sums(words, static_cast<const uint8_t *>(w), n, k, rows, hi,
+                                          mode == Q8_ACT_I8X2 ? lo : nullptr, sums, as_stream(stream)));
+}
+
+const char *q8_status_name(int status) {
+    switch (status) {
+        case Q8_OK: return "Q8_OK";
+        case Q8_E_NULL: return "Q8_E_NULL";
+        case Q8_E_SHAPE: return "Q8_E_SHAPE";
+        case Q8_E_ALIGN: return "Q8_E_ALIGN";
+        case Q8_E_MODE: return "Q8_E_MODE";
+        case Q8_E_ALIAS: return "Q8_E_ALIAS";
+        case Q8_E_HIP: return "Q8_E_HIP";
+        default: return "Q8_E_UNKNOWN";
+    }
+}
+
+int q8_version(void) { return 100; }
+
+}  // extern "C"

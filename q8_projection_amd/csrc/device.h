@@ -1,0 +1,80 @@
+// device.h -- device-side building blocks of the Q8_0 projection kernels (gfx950).
+//
+// A Q8_0 weight is consumed exactly as a checkpoint stores it: 34-byte blocks,
+// a binary16 scale then 32 int8 values (model::author page, description;
+// spatial::streamed page, description: a weight moves as it is stored).  Block g
+// of the whole matrix (row-major, g = n * nb + b) starts at byte 34 g, so odd
+// blocks start 2 bytes past a dword boundary.  Every lane loads the 9 dwords of
+// the dword-aligned window at or before its block (36 bytes, never past the end
+// of the matrix when the block count is even) and realigns the 8 quant dwords
+// with one v_perm_b32 each.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8 {
+
+constexpr int kBlock = 32;
+constexpr int kBlockBytes = 34;
+
+// The 36-byte dword-aligned window of one block.
+struct Window {
+    uint32_t d[9];
+};
+
+// Byte offset of block g's window (dword-aligned, at or before the block).
+__device__ __forceinline__ int64_t window_offset(int64_t g) { return (g * kBlockBytes) & ~int64_t(3); }
+
+// Load block g's window.  Weights are streamed once per call, so the loads
+// are non-temporal.  Needs only dword alignment of the matrix.
+__device__ __forceinline__ void load_window(const uint8_t *__restrict__ w, int64_t g, Window &out) {
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(w + window_offset(g));
+#pragma unroll
+    for (int i = 0; i < 9; ++i) out.d[i] = __builtin_nontemporal_load(p + i);
+}
+
+__device__ __forceinline__ void zero_window(Window &out) {
+#pragma unroll
+    for (int i = 0; i < 9; ++i) out.d[i] = 0u;
+}
+
+// v_perm_b32 selector that extracts quant dword j from window dwords (j, j+1):
+// even blocks start at window byte 0, their quants at byte 2; odd blocks start at
+// window byte 2, their quants at byte 4.
+__device__ __forceinline__ uint32_t window_selector(int64_t g) {
+    return (g & 1) ? 0x07060504u : 0x05040302u;
+}
+
+// Bit pattern of the block's binary16 scale.
+__device__ __forceinline__ uint32_t window_scale_bits(const Window &w, int64_t g) {
+    return (g & 1) ? (w.d[0] >> 16) : (w.d[0] & 0xffffu);
+}
+
+// The 32 int8 quants as 8 dwords (little-endian: byte i of dword j is q[4j + i]).
+__device__ __forceinline__ void window_quants(const Window &w, uint32_t sel, uint32_t (&q)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = __builtin_amdgcn_perm(w.d[j + 1], w.d[j], sel);
+}
+
+__device__ __forceinline__ float f16_bits_to_float(uint32_t bits) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+
+// Exact int32 dot product of 32 int8 pairs: 8 chained v_dot4 (|sum| <= 32*127*127).
+__device__ __forceinline__ int32_t dot32(const uint32_t (&q)[8], const uint32_t (&a)[8]) {
+    int32_t acc = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        acc = __builtin_amdgcn_sdot4(static_cast<int>(q[j]), static_cast<int>(a[j]), acc, false);
+    return acc;
+}
+
+// Sum of a double over the 64 lanes of a wave (every lane gets the total).
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+}  // namespace q8

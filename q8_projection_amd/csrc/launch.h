@@ -1,0 +1,38 @@
+// launch.h -- launchers of the HIP kernels, called by the validated C ABI.
+// Every launcher enqueues on `stream` and returns hipGetLastError()'s result.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8 {
+
+// Device facts the launchers size grids with (cached per device).
+struct DeviceInfo {
+    int cus;             // compute units
+    int lds_per_block;   // bytes of LDS one workgroup may use
+};
+DeviceInfo device_info();
+
+hipError_t launch_quantize_weights(const float *w, int64_t n, int64_t k, uint8_t *blocks,
+                                   hipStream_t stream);
+hipError_t launch_quantize_act(int words, const float *x, int64_t rows, int64_t k, int8_t *hi,
+                               int8_t *lo, float *scale, hipStream_t stream);
+
+// Projection of up to 8 rows with the int8 dot4 GEMV kernels (integer modes)
+// or the f64 GEMV (f32 mode).  mode: 0 f32, 1 one-word, 2 two-word.
+hipError_t launch_gemv(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
+                       const int8_t *lo, const float *scale, const float *x, const float *residual,
+                       float *y, hipStream_t stream);
+
+// Projection of 9..64 rows with the int8 MFMA kernel (integer modes).
+hipError_t launch_mfma(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
+                       const int8_t *lo, const float *scale, const float *residual, float *y,
+                       hipStream_t stream);
+// Whether launch_mfma serves (mode, rows).
+bool mfma_supports(int mode, int rows);
+
+hipError_t launch_block_sums(int words, const uint8_t *w, int64_t n, int64_t k, int64_t rows,
+                             const int8_t *hi, const int8_t *lo, int32_t *sums, hipStream_t stream);
+
+}  // namespace q8

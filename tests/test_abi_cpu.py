@@ -1,0 +1,125 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and every argument check returns its named status before anything is
+enqueued (no call here reaches the HIP runtime).
+
+Pointers are plain integers: validation looks at addresses only.  Every call
+here must fail a check: a call that passed validation would launch a kernel on
+these fake addresses.  Calls that pass (adjacent buffers, y == residual) are
+covered by the GPU tests with real memory.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import q8_projection_amd as q8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8.h")
+
+OK, NULL, SHAPE, ALIGN, MODE, ALIAS = 0, 1, 2, 3, 4, 5
+BASE = 0x7f0000000000        # fake, well-aligned device addresses
+MB = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q8_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert names == sorted(["q8_quantize_weights", "q8_quantize_act", "q8_matvec", "q8_matmul_rows",
+                            "q8_block_sums", "q8_status_name", "q8_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = q8.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in q8.SIGNATURES
+    assert q8.version() == 100
+
+
+def test_status_names():
+    assert [q8.status_name(i) for i in range(7)] == [q8.STATUS[i] for i in range(7)]
+    assert q8.status_name(99) == "Q8_E_UNKNOWN"
+
+
+def _mv(mode=2, w=BASE, n=64, k=256, hi=BASE + 16 * MB, lo=BASE + 32 * MB, scale=BASE + 48 * MB,
+        x=None, residual=None, y=BASE + 64 * MB, stream=None):
+    return q8.lib().q8_matvec(mode, w, n, k, hi, lo, scale, x, residual, y, stream)
+
+
+def _mm(mode=2, w=BASE, n=64, k=256, rows=4, hi=BASE + 16 * MB, lo=BASE + 32 * MB,
+        scale=BASE + 48 * MB, x=None, residual=None, y=BASE + 64 * MB):
+    return q8.lib().q8_matmul_rows(mode, w, n, k, rows, hi, lo, scale, x, residual, y, None)
+
+
+def test_empty_problems_enqueue_nothing():
+    assert _mv(n=0) == OK
+    assert _mm(rows=0) == OK
+    assert _mm(n=0) == OK
+    assert q8.lib().q8_quantize_act(2, BASE, 0, 256, BASE + MB, BASE + 2 * MB, BASE + 3 * MB, None) == OK
+    assert q8.lib().q8_quantize_weights(BASE, 0, 256, BASE + MB, None) == OK
+    assert q8.lib().q8_block_sums(1, BASE, 5, 256, 0, BASE + MB, None, BASE + 2 * MB, None) == OK
+
+
+@pytest.mark.parametrize("k", [0, -64, 32, 96, 100, 1 << 25])
+def test_bad_k(k):
+    assert _mv(k=k) == SHAPE
+    assert q8.lib().q8_quantize_act(1, BASE, 1, k, BASE + MB, None, BASE + 2 * MB, None) == SHAPE
+    assert q8.lib().q8_quantize_weights(BASE, 4, k, BASE + 8 * MB, None) == SHAPE
+
+
+def test_bad_sizes():
+    assert _mv(n=-1) == SHAPE
+    assert _mm(rows=-1) == SHAPE
+    assert _mv(n=1 << 40) == SHAPE
+
+
+def test_modes():
+    assert _mv(mode=3) == MODE
+    assert _mv(mode=-1) == MODE
+    assert q8.lib().q8_quantize_act(0, BASE, 1, 256, BASE + MB, None, BASE + 2 * MB, None) == MODE
+    assert q8.lib().q8_block_sums(0, BASE, 4, 256, 1, BASE + MB, None, BASE + 2 * MB, None) == MODE
+
+
+def test_null_pointers():
+    assert _mv(w=None) == NULL
+    assert _mv(y=None) == NULL
+    assert _mv(hi=None) == NULL
+    assert _mv(scale=None) == NULL
+    assert _mv(mode=2, lo=None) == NULL
+    assert _mv(mode=0, hi=None, lo=None, scale=None, x=None) == NULL
+    assert q8.lib().q8_quantize_act(2, BASE, 1, 256, BASE + MB, None, BASE + 2 * MB, None) == NULL
+    assert q8.lib().q8_quantize_act(1, None, 1, 256, BASE + MB, None, BASE + 2 * MB, None) == NULL
+    assert q8.lib().q8_quantize_weights(None, 4, 256, BASE + MB, None) == NULL
+
+
+def test_alignment():
+    assert _mv(w=BASE + 2) == ALIGN
+    assert _mv(hi=BASE + 16 * MB + 4) == ALIGN
+    assert _mv(lo=BASE + 32 * MB + 8) == ALIGN
+    assert _mv(scale=BASE + 48 * MB + 2) == ALIGN
+    assert _mv(y=BASE + 64 * MB + 1) == ALIGN
+    assert _mv(residual=BASE + 80 * MB + 2) == ALIGN
+    assert _mv(mode=0, hi=None, lo=None, scale=None, x=BASE + 96 * MB + 4) == ALIGN
+    assert q8.lib().q8_quantize_act(1, BASE + 4, 1, 256, BASE + MB, None, BASE + 2 * MB, None) == ALIGN
+    assert q8.lib().q8_quantize_weights(BASE + 2, 4, 256, BASE + MB, None) == ALIGN
+
+
+def test_aliasing():
+    n, k = 64, 256
+    wbytes = n * (k // 32) * 34
+    assert _mv(y=BASE + wbytes - 4) == ALIAS                    # y runs into W's last bytes
+    assert _mv(y=BASE + 16 * MB + 64) == ALIAS                  # inside hi
+    assert _mv(y=BASE + 32 * MB) == ALIAS                       # on lo
+    assert _mv(y=BASE + 48 * MB + 4) == ALIAS                   # inside scale
+    assert _mv(mode=0, hi=None, lo=None, scale=None, x=BASE + 64 * MB - 256) == ALIAS
+    r = BASE + 80 * MB
+    assert _mv(residual=r, y=r + 4) == ALIAS                    # partial overlap with residual
+    assert q8.lib().q8_quantize_act(2, BASE, 1, 256, BASE + 512, BASE + 2048, BASE + 4096, None) == ALIAS
+    assert q8.lib().q8_quantize_act(2, BASE, 1, 256, BASE + MB, BASE + MB + 128, BASE + 2 * MB, None) == ALIAS

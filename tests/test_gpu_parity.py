@@ -1,0 +1,320 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI, on the GPU.
+
+Both sides start from the same seeded f32 inputs (synth) and run the whole
+path on their own: Q8_0 weight quantization, activation quantization, the
+projection.  Quantized bytes and int32 block sums must match bit for bit; f32
+outputs must pass the gate of helpers.gate.  Every workload call is run at its
+full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import q8_projection_amd as q8
+import synth
+from synth import workloads
+
+from helpers import acts_of, gate, say, weights_of
+
+pytestmark = pytest.mark.gpu
+
+CALLS = workloads.all_calls()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    torch.cuda.set_device(0)
+    q8.lib()
+    yield
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def gpu_path(call, w_blocks_dev, x, residual=None, mode=None, out=None):
+    """GPU quantize (integer modes) and project; returns (y, hi, lo, scale) on host."""
+    mode = mode or call.mode
+    xd = to_dev(x)
+    res = None if residual is None else to_dev(residual)
+    hi = lo = sc = None
+    if mode == "f32":
+        y = q8.matmul_rows(mode, w_blocks_dev, call.n, call.k, x=xd, residual=res, out=out)
+    else:
+        hi, lo, sc = q8.quantize_act(mode, xd)
+        y = q8.matmul_rows(mode, w_blocks_dev, call.n, call.k, hi=hi, lo=lo, scale=sc, residual=res, out=out)
+    torch.cuda.synchronize()
+    cpu = lambda t: None if t is None else t.cpu().numpy()
+    return cpu(y), cpu(hi), cpu(lo), cpu(sc)
+
+
+def oracle_path(call, blocks, x, residual=None, mode=None):
+    mode = mode or call.mode
+    if mode == "f32":
+        return oracle.project(mode, blocks, call.n, call.k, x.shape[0], x=x, residual=residual), None
+    hi, lo, sc = oracle.quantize_act(mode, x)
+    return oracle.project(mode, blocks, call.n, call.k, x.shape[0], hi=hi, lo=lo, scale=sc,
+                          residual=residual), (hi, lo, sc)
+
+
+# ------------------------------------------------------------ weight quantization
+
+def _distinct_weights():
+    seen, out = set(), []
+    for c in CALLS:
+        key = (c.n, c.k, c.w_seed)
+        if key not in seen:
+            seen.add(key)
+            out.append(c)
+    return out
+
+
+@pytest.mark.parametrize("call", _distinct_weights(), ids=lambda c: f"{c.name}_w{c.w_seed}")
+def test_quantize_weights_bitwise(call):
+    say("quantize_weights", call.name, call.n, call.k, call.w_seed)
+    w, blocks = weights_of(call)
+    got = q8.quantize_weights(to_dev(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), blocks)
+
+
+@pytest.mark.parametrize("n,k,seed", [(1, 64, 40), (3, 192, 41), (37, 320, 42), (5, 2112, 43), (129, 4160, 44)])
+def test_quantize_weights_ragged(n, k, seed):
+    say("quantize_weights ragged", n, k, seed)
+    w = synth.weights(n, k, seed, outlier_frac=0.1)
+    w[0, :32] = 0.0                                     # an all-zero block
+    w[-1, -32:] *= np.float32(1e-6)                     # a block with a binary16-subnormal scale
+    got = q8.quantize_weights(to_dev(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), oracle.quantize_weights(w))
+
+
+# -------------------------------------------------------- activation quantization
+
+@pytest.mark.parametrize("call", [c for c in CALLS if c.mode != "f32"], ids=lambda c: c.name)
+def test_quantize_act_bitwise(call):
+    say("quantize_act", call.name, call.mode, call.rows, call.k)
+    x = acts_of(call)
+    hi, lo, sc = q8.quantize_act(call.mode, to_dev(x))
+    torch.cuda.synchronize()
+    ehi, elo, esc = oracle.quantize_act(call.mode, x)
+    assert np.array_equal(hi.cpu().numpy(), ehi)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), esc.view(np.uint32))
+    if call.mode == "i8x2":
+        assert np.array_equal(lo.cpu().numpy(), elo)
+
+
+def _edge_activation():
+    """Blocks that exercise rounding ties, zero and tiny scales, and huge values."""
+    x = synth.activations(3, 256, seed=77)
+    x[0, :32] = 0.0                                          # zero block
+    x[0, 32:64] = np.float32(3e-39) * synth.normal(78, 32)   # subnormal values and scale
+    x[0, 64:96] = np.float32(2.0 ** -149)                    # scale underflows to zero
+    x[1, :32] = np.arange(-16, 16, dtype=np.float32) + np.float32(0.5)   # exact ties at s = 1 ...
+    x[1, 0] = np.float32(127.0)                                          # ... (max 127 gives s = 1)
+    x[1, 32:64] = synth.normal(79, 32) * np.float32(1e30)     # huge values
+    x[2, :32] = np.float32(-1.0)                               # constant block
+    return x
+
+
+@pytest.mark.parametrize("mode", ["i8", "i8x2"])
+def test_quantize_act_edges(mode):
+    say("quantize_act edges", mode)
+    x = _edge_activation()
+    hi, lo, sc = q8.quantize_act(mode, to_dev(x))
+    torch.cuda.synchronize()
+    ehi, elo, esc = oracle.quantize_act(mode, x)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), esc.view(np.uint32))
+    assert np.array_equal(hi.cpu().numpy(), ehi)
+    if mode == "i8x2":
+        assert np.array_equal(lo.cpu().numpy(), elo)
+
+
+# ------------------------------------------------------------------ projection
+
+@pytest.mark.parametrize("call", CALLS, ids=lambda c: c.name)
+def test_projection_parity(call):
+    say("projection", call.name, call.entry, call.mode, f"rows={call.rows}", f"{call.n}x{call.k}")
+    w, blocks = weights_of(call)
+    wd = q8.quantize_weights(to_dev(w))
+    x = acts_of(call)
+    res = call.make_residual()
+    y, hi, lo, sc = gpu_path(call, wd, x, res)
+    (r, a), q = oracle_path(call, blocks, x, res)
+    assert np.array_equal(wd.cpu().numpy(), blocks)
+    if q is not None:
+        assert np.array_equal(hi, q[0]) and np.array_equal(sc.view(np.uint32), q[2].view(np.uint32))
+        if call.mode == "i8x2":
+            assert np.array_equal(lo, q[1])
+    rel, ulps = gate(y, r, a, call.name)
+    say("projection", call.name, f"max rel err {rel:.3g}", f"max ulps {ulps}")
+
+
+def test_matvec_entry_point():
+    """q8_matvec is the rows == 1 projection: same bits as q8_matmul_rows."""
+    call = workloads.attn()[0]
+    say("matvec entry", call.name)
+    w, blocks = weights_of(call)
+    wd = to_dev(blocks)
+    x = acts_of(call)
+    res = to_dev(call.make_residual())
+    hi, lo, sc = q8.quantize_act(call.mode, to_dev(x))
+    y1 = q8.matvec(call.mode, wd, call.n, call.k, hi=hi[0], lo=lo[0], scale=sc[0], residual=res[0])
+    y2 = q8.matmul_rows(call.mode, wd, call.n, call.k, hi=hi, lo=lo, scale=sc, residual=res)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2[0])
+
+
+# ------------------------------------------------------------------ block sums
+
+@pytest.mark.parametrize("mode", ["i8", "i8x2"])
+@pytest.mark.parametrize("n,k,rows", [(256, 1024, 1), (4096, 4096, 1), (37, 2112, 3), (300, 4096, 8),
+                                      (64, 14336, 2)])
+def test_block_sums_bitwise(mode, n, k, rows):
+    say("block_sums", mode, n, k, rows)
+    w = synth.weights(n, k, seed=90 + rows, outlier_frac=0.01)
+    x = synth.activations(rows, k, seed=95 + rows, outlier_frac=0.005)
+    blocks = oracle.quantize_weights(w)
+    hi, lo, sc = oracle.quantize_act(mode, x)
+    got = q8.block_sums(mode, to_dev(blocks), n, k, to_dev(hi), None if lo is None else to_dev(lo))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), oracle.block_sums(mode, blocks, n, k, hi, lo))
+
+
+# ------------------------------------------------------------ ragged and edges
+
+@pytest.mark.parametrize("mode", ["f32", "i8", "i8x2"])
+@pytest.mark.parametrize("n,k,rows", [(1, 64, 1), (3, 192, 2), (7, 2112, 3), (13, 4160, 5), (37, 320, 8),
+                                      (29, 1024, 9), (17, 512, 12), (11, 256, 64), (5, 128, 65),
+                                      (130, 4096, 7)])
+def test_ragged_shapes(mode, n, k, rows):
+    say("ragged", mode, n, k, rows)
+    w = synth.weights(n, k, seed=200 + n, outlier_frac=0.1)
+    x = synth.activations(rows, k, seed=300 + k, outlier_frac=0.05)
+    res = synth.normal(400 + rows, (rows, n))
+    blocks = oracle.quantize_weights(w)
+    call = workloads.Call("ragged", n, k, rows, mode, "matmul_rows", w_seed=0)
+    y, *_ = gpu_path(call, to_dev(blocks), x, res)
+    (r, a), _ = oracle_path(call, blocks, x, res)
+    gate(y, r, a, f"ragged {mode} {n}x{k} rows={rows}")
+
+
+def test_stack_rows_equal_single_rows():
+    """Within the GEMV family a stacked row gives the same bits as that row alone
+    (same block order, same reductions)."""
+    n, k = 515, 4096
+    say("stack vs single rows", n, k)
+    w = synth.weights(n, k, seed=501)
+    x = synth.activations(8, k, seed=502)
+    wd = to_dev(oracle.quantize_weights(w))
+    for mode in ("i8", "i8x2", "f32"):
+        xd = to_dev(x)
+        if mode == "f32":
+            ys = q8.matmul_rows(mode, wd, n, k, x=xd)
+            singles = [q8.matvec(mode, wd, n, k, x=xd[r]) for r in range(8)]
+        else:
+            hi, lo, sc = q8.quantize_act(mode, xd)
+            ys = q8.matmul_rows(mode, wd, n, k, hi=hi, lo=lo, scale=sc)
+            singles = [q8.matvec(mode, wd, n, k, hi=hi[r], lo=None if lo is None else lo[r], scale=sc[r])
+                       for r in range(8)]
+        torch.cuda.synchronize()
+        for r in range(8):
+            assert torch.equal(ys[r], singles[r]), (mode, r)
+
+
+def test_inplace_residual_and_adjacent_buffers():
+    n, k, rows = 1000, 2048, 4
+    say("in-place residual", n, k, rows)
+    w = synth.weights(n, k, seed=601)
+    x = synth.activations(rows, k, seed=602)
+    res = synth.normal(603, (rows, n))
+    wd = to_dev(oracle.quantize_weights(w))
+    hi, lo, sc = q8.quantize_act("i8x2", to_dev(x))
+    y_sep = q8.matmul_rows("i8x2", wd, n, k, hi=hi, lo=lo, scale=sc, residual=to_dev(res))
+    buf = torch.empty(2 * rows * n, dtype=torch.float32, device="cuda")
+    inplace = buf[:rows * n].view(rows, n)                      # y == residual, with y's
+    inplace.copy_(to_dev(res))                                  # neighbour right after it
+    q8.matmul_rows("i8x2", wd, n, k, hi=hi, lo=lo, scale=sc, residual=inplace, out=inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(inplace, y_sep)
+
+
+def test_outputs_stay_in_bounds():
+    """Canary words around every output are left untouched."""
+    n, k, rows = 333, 1088, 6
+    say("canaries", n, k, rows)
+    w = synth.weights(n, k, seed=701)
+    x = synth.activations(rows, k, seed=702)
+    pad = 4096
+    canary = -7.77e33
+    wd = to_dev(oracle.quantize_weights(w))
+    for mode in ("f32", "i8", "i8x2"):
+        yb = torch.full((rows * n + 2 * pad,), canary, dtype=torch.float32, device="cuda")
+        y = yb[pad:pad + rows * n].view(rows, n)
+        xd = to_dev(x)
+        if mode == "f32":
+            q8.matmul_rows(mode, wd, n, k, x=xd, out=y)
+        else:
+            hb = torch.full((rows * k + 2 * pad,), 99, dtype=torch.int8, device="cuda")
+            lb = torch.full((rows * k + 2 * pad,), 99, dtype=torch.int8, device="cuda")
+            sb = torch.full((rows * (k // 32) + 2 * pad,), canary, dtype=torch.float32, device="cuda")
+            hi = hb[pad:pad + rows * k].view(rows, k)
+            lo = lb[pad:pad + rows * k].view(rows, k) if mode == "i8x2" else None
+            sc = sb[pad:pad + rows * (k // 32)].view(rows, k // 32)
+            q8.quantize_act(mode, xd, hi=hi, lo=lo, scale=sc)
+            q8.matmul_rows(mode, wd, n, k, hi=hi, lo=lo, scale=sc, out=y)
+            torch.cuda.synchronize()
+            for t, c in ((hb, 99), (lb, 99)):
+                assert (t[:pad] == c).all() and (t[-pad:] == c).all()
+            assert (sb[:pad] == canary).all() and (sb[-pad:] == canary).all()
+        torch.cuda.synchronize()
+        assert (yb[:pad] == canary).all() and (yb[-pad:] == canary).all(), mode
+        assert torch.isfinite(y).all()
+
+
+def test_empty_problems_touch_nothing():
+    say("empty problems")
+    y = torch.full((4, 8), 3.0, device="cuda")
+    wd = torch.zeros(8 * 34 * 2, dtype=torch.uint8, device="cuda")
+    hi = torch.zeros((4, 64), dtype=torch.int8, device="cuda")
+    sc = torch.zeros((4, 2), dtype=torch.float32, device="cuda")
+    q8.matmul_rows("i8", wd, 8, 64, hi=hi, scale=sc, out=y, rows=0)
+    q8.matmul_rows("i8", wd, 0, 64, hi=hi, scale=sc, out=y, rows=4)
+    torch.cuda.synchronize()
+    assert (y == 3.0).all()
+
+
+def _hip():
+    import ctypes
+    h = ctypes.CDLL("libamdhip64.so")
+    h.hipHostGetDevicePointer.restype = ctypes.c_int
+    h.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+    return h
+
+
+def test_host_mapped_weights_same_bits():
+    """Where the weight lives changes no value (codegen_cuda::lane page, Modules:
+    residence): W in pinned host memory, read through the device address the
+    runtime maps it to, gives the same bits as W in device memory."""
+    import ctypes
+    n, k = 257, 2048
+    say("host-mapped weights", n, k)
+    w = synth.weights(n, k, seed=801)
+    x = synth.activations(2, k, seed=802)
+    blocks = oracle.quantize_weights(w)
+    w_dev = to_dev(blocks)
+    w_host = torch.from_numpy(blocks).pin_memory()
+    dptr = ctypes.c_void_p()
+    if _hip().hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(w_host.data_ptr()), 0) != 0 or not dptr.value:
+        pytest.skip("pinned host memory has no device mapping here")
+    hi, lo, sc = q8.quantize_act("i8x2", to_dev(x))
+    y_dev = q8.matmul_rows("i8x2", w_dev, n, k, hi=hi, lo=lo, scale=sc)
+    y_host = torch.empty_like(y_dev)
+    st = q8.lib().q8_matmul_rows(2, dptr, n, k, 2, ctypes.c_void_p(hi.data_ptr()), ctypes.c_void_p(lo.data_ptr()),
+                                 ctypes.c_void_p(sc.data_ptr()), None, None, ctypes.c_void_p(y_host.data_ptr()),
+                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(y_dev, y_host)
