@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Throughput of the Q8_0 projection hot path on one MI355X.
+
+One step is one pass over every stage of the path, at the shapes the pages'
+model forms run (codegen_cuda::lane page, description: decode steps, batched
+decode, prefill chunks; model::author page, Functions: prefill, decode_batch):
+
+  rows = 1   down projection   W 4096 x 14336, two-word   (quantize + q8_matvec)
+  rows = 8   batched decode    W 14336 x 4096, two-word   (quantize + q8_matmul_rows)
+  rows = 8   batched decode    W 4096 x 14336, two-word, residual epilogue
+  rows = 64  prefill chunk     W 14336 x 4096, one-word   (quantize + q8_matmul_rows)
+  rows = 1   LM head           W 151936 x 2048, one-word, the chunk's last row
+
+Each call quantizes its activation rows on the GPU, then projects.  Weights are
+synthetic (seeded, N(0, 0.02^2)), Q8_0-quantized on the GPU before timing and
+resident in HBM.  Every matrix has two copies and consecutive steps alternate
+between them.  A step then reads about 580 MB of distinct weights, so the 256 MB
+Infinity Cache cannot serve a weight from the previous step.  The step is
+captured in a HIP graph and replayed, as the lane replays each step
+(codegen_cuda::lane page, description).
+
+value = weight bytes of one step / step time (GB/s).  The JSON line also carries
+per-call kernel times, the rows=1/8/64 bandwidths, the roofline of the dominant
+kernel and the CPU oracle's throughput on a sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "Q8_0 projection effective weight GB/s and % HBM peak at rows=1/8/64"
+COUNTERS = os.path.join(ROOT, "profiles", "lm_head_gemv_counters.txt")
+KERNEL_SOURCES = ["q8_projection_amd/csrc/gemv.hip", "q8_projection_amd/csrc/device.h"]
+
+
+def step_calls():
+    from synth import workloads as wl
+    by_name = {c.name: c for c in wl.all_calls()}
+    return [by_name["down_i8x2"], by_name["batch8"], by_name["batch8_down_res"], by_name["prefill64"],
+            by_name["lm_head"]]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if it is missing or was taken on other kernel sources."""
+    try:
+        fields = {}
+        with open(COUNTERS) as f:
+            for line in f:
+                if "=" in line and not line.lstrip().startswith("#"):
+                    k, v = line.split("=", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("kernel_sources_sha256_16") != kernel_hash():
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+class Prepared:
+    """Device buffers of one call: weight copies, activations, outputs."""
+
+    def __init__(self, call, dev):
+        import numpy as np
+        import torch
+        import q8_projection_amd as q8
+        self.call = call
+        # enough copies that cycling through them reads over 512 MiB between
+        # two uses of one copy: none can be served from the Infinity Cache
+        self.copies = max(2, -(-(512 << 20) // call.weight_bytes))
+        w = torch.from_numpy(call.make_weights()).to(dev)
+        self.w = [q8.quantize_weights(w) for _ in range(self.copies)]
+        del w
+        x = call.make_activations()
+        self.x = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        res = call.make_residual()
+        self.res = None if res is None else torch.from_numpy(res).to(dev)
+        rows, k, n = call.rows, call.k, call.n
+        self.hi = torch.empty((rows, k), dtype=torch.int8, device=dev)
+        self.lo = torch.empty((rows, k), dtype=torch.int8, device=dev) if call.mode == "i8x2" else None
+        self.sc = torch.empty((rows, k // 32), dtype=torch.float32, device=dev)
+        self.y = torch.empty((rows, n), dtype=torch.float32, device=dev)
+
+    def quantize(self):
+        import q8_projection_amd as q8
+        q8.quantize_act(self.call.mode, self.x, hi=self.hi, lo=self.lo, scale=self.sc)
+
+    def project(self, copy):
+        import q8_projection_amd as q8
+        c = self.call
+        if c.rows == 1:
+            q8.matvec(c.mode, self.w[copy], c.n, c.k, hi=self.hi[0], lo=None if self.lo is None else self.lo[0],
+                      scale=self.sc[0], residual=None if self.res is None else self.res[0], out=self.y[0])
+        else:
+            q8.matmul_rows(c.mode, self.w[copy], c.n, c.k, hi=self.hi, lo=self.lo, scale=self.sc,
+                           residual=self.res, out=self.y)
+
+
+def capture(fn, reps=1):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm the path on the capture stream once
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(reps):
+                fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, iters):
+    """Mean GPU time of one replay, from HIP events on the replay stream."""
+    import torch
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(iters):
+        g.replay()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters * 1e-3  # seconds
+
+
+def cpu_baseline(calls, budget_s: float):
+    """The oracle on the host: activation quantization and projection of the same
+    calls, on every 16th weight row (full K, all activation rows)."""
+    import numpy as np
+    import oracle
+    import synth
+    stride = 16
+    work = []
+    for c in calls:
+        rows_sel = np.arange(0, c.n, stride)
+        w = np.empty((rows_sel.size, c.k), dtype=np.float32)
+        for i, r in enumerate(rows_sel):
+            w[i] = synth.normal(c.w_seed, c.k, 0.02, offset=int(r) * c.k)
+        if c.w_outlier_frac:
+            raise ValueError("sampled weights do not model outlier rows")
+        blocks = oracle.quantize_weights(w)
+        x = c.make_activations()
+        res = c.make_residual()
+        res_s = None if res is None else np.ascontiguousarray(res[:, rows_sel])
+        work.append((c, blocks, x, res_s, rows_sel.size))
+    sample_bytes = sum(n_s * (c.k // 32) * 34 for c, _, _, _, n_s in work)
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        for c, blocks, x, res_s, n_s in work:
+            if c.mode == "f32":
+                oracle.project(c.mode, blocks, n_s, c.k, x.shape[0], x=x, residual=res_s)
+            else:
+                hi, lo, sc = oracle.quantize_act(c.mode, x)
+                oracle.project(c.mode, blocks, n_s, c.k, x.shape[0], hi=hi, lo=lo, scale=sc, residual=res_s)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() > t_end or len(times) >= 50:
+            break
+    med = sorted(times)[len(times) // 2]
+    return {
+        "value": round(sample_bytes / med / 1e9, 3),
+        "unit": "GB/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"every {stride}th weight row of each call of the step (full K, all activation rows), "
+                  f"{sample_bytes / 1e6:.1f} MB of Q8_0 weights; activation quantization + projection; "
+                  f"median of {len(times)} passes",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default=None, help="run only the named call eagerly (for profilers)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (a projection's share of a "
+              "sharded layer is the same kernel at its own shape)", file=sys.stderr)
+        return 2
+
+    import torch
+    import q8_projection_amd as q8
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    q8.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    calls = step_calls()
+    copies = 2  # the step graphs alternate two copies of every matrix
+    prepared = [Prepared(c, dev) for c in calls]
+    torch.cuda.synchronize()
+
+    if args.only:
+        p = next(p for p in prepared if p.call.name == args.only)
+        p.quantize()
+        for i in range(args.warmup + args.steps):
+            p.project(i % p.copies)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "launches": args.warmup + args.steps}))
+        return 0
+
+    def step(copy):
+        for p in prepared:
+            p.quantize()
+            p.project(copy)
+
+    # eager reference outputs, then the graphs; every replay must reproduce them
+    step(0)
+    torch.cuda.synchronize()
+    ref = [p.y.clone() for p in prepared]
+    graphs = [capture(lambda c=c: step(c)) for c in range(copies)]
+    for g in graphs:
+        for p in prepared:
+            p.y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for p, r in zip(prepared, ref):
+            if not torch.equal(p.y, r):
+                raise RuntimeError(f"graph replay differs from the eager step in {p.call.name}")
+
+    for i in range(args.warmup):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    step_s = elapsed / args.steps
+    step_bytes = sum(c.weight_bytes for c in calls)
+
+    # per-call kernel times: a graph of back-to-back launches cycling the copies
+    per_call = {}
+    reps = 20
+    for p in prepared:
+        p.quantize()
+        gq = capture(lambda p=p: p.quantize(), reps)
+        gp = capture(lambda p=p: [p.project(i % p.copies) for i in range(reps)])
+        tq = time_graph(gq, 5) / reps
+        tp = time_graph(gp, 5) / reps
+        per_call[p.call.name] = {"rows": p.call.rows, "n": p.call.n, "k": p.call.k, "mode": p.call.mode,
+                                 "weight_bytes": p.call.weight_bytes,
+                                 "project_us": round(tp * 1e6, 3), "quantize_us": round(tq * 1e6, 3),
+                                 "GBps": round(p.call.weight_bytes / tp / 1e9, 1),
+                                 "pct_hbm_peak": round(p.call.weight_bytes / tp / 1e9 / HBM_PEAK_GBPS * 100, 1),
+                                 "rows_GFLOPs": round(p.call.flops / tp / 1e9, 1)}
+    by_rows = {}
+    for name, d in per_call.items():
+        key = str(d["rows"])
+        agg = by_rows.setdefault(key, {"bytes": 0, "us": 0.0})
+        agg["bytes"] += d["weight_bytes"]
+        agg["us"] += d["project_us"]
+    per_rows = {k: {"GBps": round(v["bytes"] / v["us"] / 1e3, 1),
+                    "pct_hbm_peak": round(v["bytes"] / v["us"] / 1e3 / HBM_PEAK_GBPS * 100, 1)}
+                for k, v in by_rows.items()}
+
+    dom_name = max(per_call, key=lambda n: per_call[n]["project_us"])
+    dom = per_call[dom_name]
+    achieved = dom["weight_bytes"] / (dom["project_us"] * 1e-6) / 1e9
+    traffic = stored_traffic() if dom_name == "lm_head" else None
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": f"{dom_name}: rows={dom['rows']} {dom['n']}x{dom['k']} {dom['mode']}",
+                "algorithmic_bytes": dom["weight_bytes"]}
+
+    cpu = None if args.no_cpu else cpu_baseline(calls, args.cpu_budget)
+
+    out = {
+        "metric": METRIC,
+        "value": round(step_bytes / step_s / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": "Q8_0 projection step: decode rows=1 (4096x14336, two-word) + batched decode "
+                               "rows=8 (14336x4096 two-word; 4096x14336 two-word + residual) + prefill rows=64 "
+                               "(14336x4096, one-word) + LM head on the last row (151936x2048, one-word)",
+                   "weight_bytes_per_step": step_bytes, "graph_replay": True,
+                   "weight_copies": {p.call.name: p.copies for p in prepared}},
+        "pct_hbm_peak": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBPS * 100, 1),
+        "per_rows": per_rows,
+        "per_call": per_call,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

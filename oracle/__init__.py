@@ -58,6 +58,7 @@ def _load():
             "q8ref_project_at": (_I, [_I, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64, _P, _P,
                                       _P, _P]),
             "q8ref_dense_matvec": (None, [_P, _I64, _I64, _I64, _P, _P]),
+            "q8ref_threads": (_I, []),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -65,6 +66,11 @@ def _load():
             fn.argtypes = args
         _lib = lib
     return _lib
+
+
+def threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(_load().q8ref_threads())
 
 
 def _ptr(a):

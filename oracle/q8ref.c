@@ -318,3 +318,11 @@ void q8ref_rha_array(const float *x, int64_t count, float *out) {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < count; ++i) out[i] = rha(x[i]);
 }
+
+/* Threads the OpenMP loops above use. */
+#ifdef _OPENMP
+#include <omp.h>
+int q8ref_threads(void) { return omp_get_max_threads(); }
+#else
+int q8ref_threads(void) { return 1; }
+#endif

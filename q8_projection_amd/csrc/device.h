@@ -26,12 +26,12 @@ struct Window {
 // Byte offset of block g's window (dword-aligned, at or before the block).
 __device__ __forceinline__ int64_t window_offset(int64_t g) { return (g * kBlockBytes) & ~int64_t(3); }
 
-// Load block g's window.  Weights are streamed once per call, so the loads
-// are non-temporal.  Needs only dword alignment of the matrix.
+// Load block g's window with the default cache policy (for this access pattern
+// the non-temporal hint measured slower).  Needs only dword alignment.
 __device__ __forceinline__ void load_window(const uint8_t *__restrict__ w, int64_t g, Window &out) {
     const uint32_t *p = reinterpret_cast<const uint32_t *>(w + window_offset(g));
 #pragma unroll
-    for (int i = 0; i < 9; ++i) out.d[i] = __builtin_nontemporal_load(p + i);
+    for (int i = 0; i < 9; ++i) out.d[i] = p[i];
 }
 
 __device__ __forceinline__ void zero_window(Window &out) {
@@ -70,11 +70,33 @@ __device__ __forceinline__ int32_t dot32(const uint32_t (&q)[8], const uint32_t 
     return acc;
 }
 
-// Sum of a double over the 64 lanes of a wave (every lane gets the total).
+// One DPP move of a double (each 32-bit half moved with the same control).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b), CTRL, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, 0xf, 0xf, false);
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                          static_cast<uint32_t>(lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(b), lane);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane);
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Sum of a double over the 64 lanes of a wave, in a fixed order; every lane
+// gets the total.  Within each 16-lane row: pairs, quads (quad_perm), halves
+// (row_half_mirror), the row (row_mirror); then the four row sums read out of
+// lanes 0, 16, 32, 48.  No LDS round trips.
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v += dpp_f64<0xb1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f64<0x4e>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f64<0x141>(v);  // row_half_mirror
+    v += dpp_f64<0x140>(v);  // row_mirror
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 }  // namespace q8

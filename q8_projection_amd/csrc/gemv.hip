@@ -1,16 +1,29 @@
-// gemv.hip -- the projection for stacks of 1..8 activation rows: wave64 GEMV
-// over Q8_0 weights.
+// gemv.hip -- the projection for stacks of 1..8 activation rows: a wave64
+// GEMV over Q8_0 weights.
 //
 // Each weight row is streamed from HBM once for the whole stack (codegen_cuda::
 // lane page, description: every projection reads its weights once for the
 // block; model::author page, Functions: decode_batch).  The pages' own kernel
 // runs four output rows a (32-wide) warp (codegen_cuda::lane page, Modules,
-// plan: rows_a_warp); here a 64-wide wave owns MR output rows and its lanes
-// stride over the rows' 34-byte blocks, so one wave-wide load instruction covers
-// 64 consecutive blocks (2176 contiguous bytes).  The activation stack (int8
-// words and block scales, or f32 values) is staged once per workgroup in LDS and
-// read back per block.  Integer modes take exact int32 block sums with v_dot4;
-// every block term is accumulated in f64 and each output is rounded once.
+// plan: rows_a_warp).  Here a 64-wide wave owns a group of MR output rows at a
+// time.  Its lanes stride over the rows' 34-byte blocks, so one wave-wide load
+// covers 64 consecutive blocks (2176 contiguous bytes).
+//
+// Resident kernels (the activation stack fits in LDS): the grid is persistent and
+// each wave walks a sequence of items (row group, 64-block column).  A register
+// ring keeps P items of weight windows in flight.  Weight windows are read with
+// range-checked buffer loads: a lane or item outside the matrix reads zeros
+// without touching memory and without a branch, so every item issues the same
+// loads and the wait counts stay exact.  For the same reason the main loop
+// holds no other vector-memory operation: each row's f64 total goes to LDS, and
+// the residual add and the f32 store run after the loop.
+//
+// Tiled kernels (the stack is too large for LDS): the stack is staged in column
+// tiles between barriers and each wave owns one row group.
+//
+// The activation stack (int8 words and block scales, or f32 values) is staged
+// with direct-to-LDS loads.  Integer modes take exact int32 block sums with
+// v_dot4; every block term is accumulated in f64 and each output is rounded once.
 #include <algorithm>
 
 #include "device.h"
@@ -21,6 +34,16 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kLdsBudget = 64 * 1024;     // LDS for the staged stack, per workgroup
+constexpr int kOutPerWave = 128;          // f64 totals a wave may park in LDS
+constexpr int kTiledMaxUb = 4;            // 64-block columns per tile in the tiled kernels
+constexpr uint32_t kBufferDword3 = 0x00020000u;  // raw buffer resource, gfx9 family
+constexpr uint32_t kOob = 0x80000000u;    // an offset past every range: reads return 0
+constexpr int64_t kMaxStreamBytes = int64_t(1) << 30;  // weight bytes one resident launch streams
+constexpr int kLoadsPerWindow = 3;       // buffer loads issue_item makes per window
+constexpr int kLoadPolicy = 0;            // cache policy of the weight stream (default: measured fastest)
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct GemvArgs {
     const uint8_t *w;       // Q8_0 blocks [n][nb]
@@ -30,283 +53,472 @@ struct GemvArgs {
     const float *x;         // [rows][k] (f32 mode)
     const float *residual;  // [rows][n] or null
     float *y;               // [rows][n]
-    int64_t n;
+    int64_t n;              // weight rows of this launch
+    int64_t ldy;            // row stride of y and residual (elements)
     int k;
     int nb;
-    int kt;                 // columns per LDS tile (multiple of 256)
-    int64_t num_groups;     // row groups of kWaves * MR rows
+    int kt;                 // columns per LDS tile (a multiple of 64); kt == k: resident
+    int ntiles;
+    int ub;                 // 64-block columns per tile
+    int64_t num_groups;     // row groups of MR rows
 };
 
-// ---------------------------------------------------------------- integer modes
+// ------------------------------------------------------------------ staging
 
-// LDS tile layout: hi [R][kt] bytes, lo [R][kt] bytes (two-word), then the block
-// scales [R][kt/32] as f64 (divided by 128 in two-word mode, exact).
-template <int R, int WORDS>
-__device__ __forceinline__ void stage_int_tile(const GemvArgs &a, uint8_t *lds, int kt0, int ktc) {
-    const int tid = threadIdx.x;
-    const int vec_per_row = ktc / 16;
-    int8_t *lhi = reinterpret_cast<int8_t *>(lds);
-    int8_t *llo = lhi + R * a.kt;
-    double *ls = reinterpret_cast<double *>(lhi + WORDS * R * a.kt);
-    for (int i = tid; i < R * vec_per_row; i += kThreads) {
-        const int r = i / vec_per_row, c = (i % vec_per_row) * 16;
-        *reinterpret_cast<uint4 *>(lhi + r * a.kt + c) =
-            *reinterpret_cast<const uint4 *>(a.hi + static_cast<int64_t>(r) * a.k + kt0 + c);
-        if (WORDS == 2)
-            *reinterpret_cast<uint4 *>(llo + r * a.kt + c) =
-                *reinterpret_cast<const uint4 *>(a.lo + static_cast<int64_t>(r) * a.k + kt0 + c);
-    }
-    const int tbk = ktc / kBlock, kb0 = kt0 / kBlock, ktb = a.kt / kBlock;
-    for (int i = tid; i < R * tbk; i += kThreads) {
-        const int r = i / tbk, b = i % tbk;
-        const double s = static_cast<double>(a.scale[static_cast<int64_t>(r) * a.nb + kb0 + b]);
-        ls[r * ktb + b] = (WORDS == 2) ? s * (1.0 / 128.0) : s;
+// The activation stack is copied into LDS with gfx950's direct-to-LDS loads
+// (global_load_lds_dwordx4 / _dword): the data never passes through VGPRs.  One
+// wave-wide instruction moves one chunk (64 lanes x 16 or 4 bytes) to a
+// wave-uniform LDS address; chunks are dealt round-robin to the workgroup's
+// waves.  Callers wait for the copies (vmcnt) and then barrier.
+
+typedef __attribute__((address_space(1))) const void *gptr_t;
+typedef __attribute__((address_space(3))) void *lptr_t;
+
+// rows x bytes (bytes a multiple of 16) from src (row stride src_stride) to LDS
+// dst (row stride dst_stride), 16 bytes per lane.
+__device__ __forceinline__ void dma_rows16(uint8_t *dst, int dst_stride, const uint8_t *src, int64_t src_stride,
+                                           int rows, int bytes, int wave, int lane) {
+    const int per_row = (bytes + 1023) / 1024;
+    for (int c = wave; c < rows * per_row; c += kWaves) {
+        const int r = c / per_row, off = (c - r * per_row) * 1024;
+        if (off + lane * 16 < bytes)
+            __builtin_amdgcn_global_load_lds((gptr_t)(src + r * src_stride + off + lane * 16),
+                                             (lptr_t)(dst + r * dst_stride + off), 16, 0, 0);
     }
 }
 
-template <int R, int WORDS, int MR, int U>
-__global__ __launch_bounds__(kThreads) void gemv_int_kernel(GemvArgs a) {
-    extern __shared__ __align__(16) uint8_t lds[];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+// rows x count f32 values from src (row stride src_stride floats) to LDS dst
+// (row stride dst_stride floats), one dword per lane.
+__device__ __forceinline__ void dma_rows4(float *dst, int dst_stride, const float *src, int64_t src_stride,
+                                          int rows, int count, int wave, int lane) {
+    const int per_row = (count + 63) / 64;
+    for (int c = wave; c < rows * per_row; c += kWaves) {
+        const int r = c / per_row, off = (c - r * per_row) * 64;
+        if (off + lane < count)
+            __builtin_amdgcn_global_load_lds((gptr_t)(src + r * src_stride + off + lane),
+                                             (lptr_t)(dst + r * dst_stride + off), 4, 0, 0);
+    }
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding,
+// then barrier.  The direct-to-LDS copies of a tile are issued before the N
+// weight loads that follow them, and vmcnt retires in order, so after the wait
+// this wave's copies have landed while its weight loads stay in flight; after
+// the barrier every wave's copies have.  A bare s_barrier is used: the fences of
+// __syncthreads would make the compiler wait for the weight loads too.
+template <int N>
+__device__ __forceinline__ void staged_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    // s_waitcnt fields (gfx9): vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]
+    __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | 0x70 | 0xf00);
+    __builtin_amdgcn_s_barrier();
+}
+
+// Integer modes.  LDS: hi [R][kt] bytes, lo [R][kt] bytes (two-word), scales [R][kt/32] f32.
+template <int R, int WORDS>
+__device__ __forceinline__ void stage_int(const GemvArgs &a, uint8_t *lds, int ti, int wave, int lane) {
+    const int kt0 = ti * a.kt, ktc = min(a.kt, a.k - kt0);
+    dma_rows16(lds, a.kt, reinterpret_cast<const uint8_t *>(a.hi) + kt0, a.k, R, ktc, wave, lane);
+    if (WORDS == 2)
+        dma_rows16(lds + R * a.kt, a.kt, reinterpret_cast<const uint8_t *>(a.lo) + kt0, a.k, R, ktc, wave, lane);
+    dma_rows4(reinterpret_cast<float *>(lds + WORDS * R * a.kt), a.kt / kBlock, a.scale + kt0 / kBlock, a.nb, R,
+              ktc / kBlock, wave, lane);
+}
+
+// f32 mode.  LDS: x [R][kt] f32.
+template <int R>
+__device__ __forceinline__ void stage_f32(const GemvArgs &a, uint8_t *lds, int ti, int wave, int lane) {
+    const int kt0 = ti * a.kt, ktc = min(a.kt, a.k - kt0);
+    dma_rows16(lds, a.kt * 4, reinterpret_cast<const uint8_t *>(a.x + kt0), static_cast<int64_t>(a.k) * 4, R,
+               ktc * 4, wave, lane);
+}
+
+// ------------------------------------------------------------- weight windows
+
+// One item: row group grp, tile ti, 64-block column u (lane's block bl = u*64 + lane).
+struct Item {
+    int64_t grp;
+    int ti;
+    int u;
+};
+
+// Load the item's MR windows with range-checked buffer loads.  `live` is false
+// for ring refills past the wave's last item: every lane then reads zeros.
+template <int MR>
+__device__ __forceinline__ void issue_item(const GemvArgs &a, const Item &it, bool live, int lane,
+                                           Window (&win)[MR]) {
+    const int ktb = a.kt / kBlock;
+    const int kb0 = it.ti * ktb;
+    const int nbt = min(ktb, a.nb - kb0);
+    const int bl = it.u * 64 + lane;
+    const int64_t row0 = it.grp * MR;
+    const int64_t left = a.n - row0;
+    const int rows_here = live ? static_cast<int>(left < 0 ? 0 : (left > MR ? MR : left)) : 0;
+    const uint8_t *base = rows_here > 0 ? a.w + row0 * a.nb * kBlockBytes : a.w;
+    const uint32_t range = static_cast<uint32_t>(rows_here) * static_cast<uint32_t>(a.nb) * kBlockBytes;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, static_cast<int>(range), kBufferDword3);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        const bool ok = bl < nbt && m < rows_here;
+        const uint32_t off =
+            ok ? static_cast<uint32_t>(window_offset(static_cast<int64_t>(m) * a.nb + kb0 + bl)) : kOob;
+        const u32x4 d0 = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kLoadPolicy);
+        const u32x4 d1 = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 16, 0, kLoadPolicy);
+        const uint32_t d2 = __builtin_amdgcn_raw_buffer_load_b32(rsrc, off + 32, 0, kLoadPolicy);
+        win[m].d[0] = d0.x; win[m].d[1] = d0.y; win[m].d[2] = d0.z; win[m].d[3] = d0.w;
+        win[m].d[4] = d1.x; win[m].d[5] = d1.y; win[m].d[6] = d1.z; win[m].d[7] = d1.w;
+        win[m].d[8] = d2;
+    }
+}
+
+// ------------------------------------------------------------------- compute
+
+// Integer modes: acc[m][r] += d * s * T with T = S_hi (one-word) or
+// 128 S_hi + S_lo (two-word; the 1/128 is applied to the total, exactly).
+template <int R, int WORDS, int MR>
+__device__ __forceinline__ void compute_int_item(const GemvArgs &a, const uint8_t *lds, const Item &it, int lane,
+                                                 const Window (&win)[MR], double (&acc)[MR][R]) {
+    const int ktb = a.kt / kBlock;
+    const int kb0 = it.ti * ktb;
+    const int nbt = min(ktb, a.nb - kb0);
+    const int bl = it.u * 64 + lane;
+    if (bl >= nbt) return;
     const int8_t *lhi = reinterpret_cast<const int8_t *>(lds);
     const int8_t *llo = lhi + R * a.kt;
-    const double *ls = reinterpret_cast<const double *>(lhi + WORDS * R * a.kt);
+    const float *ls = reinterpret_cast<const float *>(lhi + WORDS * R * a.kt);
+    // The block's parity is all the realignment needs: nb and kb0 are even, so
+    // block (grp*MR + m, kb0 + bl) has the parity of bl.
+    const uint32_t sel = window_selector(bl);
+    uint32_t q[MR][8];
+    double d[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        window_quants(win[m], sel, q[m]);
+        d[m] = static_cast<double>(f16_bits_to_float(window_scale_bits(win[m], bl)));
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        uint32_t h[8], l[8];
+        const uint4 *ph = reinterpret_cast<const uint4 *>(lhi + r * a.kt + bl * kBlock);
+        const uint4 h0 = ph[0], h1 = ph[1];
+        h[0] = h0.x; h[1] = h0.y; h[2] = h0.z; h[3] = h0.w;
+        h[4] = h1.x; h[5] = h1.y; h[6] = h1.z; h[7] = h1.w;
+        if (WORDS == 2) {
+            const uint4 *pl = reinterpret_cast<const uint4 *>(llo + r * a.kt + bl * kBlock);
+            const uint4 l0 = pl[0], l1 = pl[1];
+            l[0] = l0.x; l[1] = l0.y; l[2] = l0.z; l[3] = l0.w;
+            l[4] = l1.x; l[5] = l1.y; l[6] = l1.z; l[7] = l1.w;
+        }
+        const double s = static_cast<double>(ls[r * ktb + bl]);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            int32_t t = dot32(q[m], h);
+            if (WORDS == 2) t = t * 128 + dot32(q[m], l);
+            acc[m][r] += (d[m] * s) * static_cast<double>(t);
+        }
+    }
+}
+
+// f32 mode: acc[0][r] += d * sum_j q_j x_j, every product and sum in f64.
+template <int R, int MR>
+__device__ __forceinline__ void compute_f64_item(const GemvArgs &a, const uint8_t *lds, const Item &it, int lane,
+                                                 const Window (&win)[MR], double (&acc)[MR][R]) {
+    static_assert(MR == 1, "the f32 mode runs one weight row a wave");
     const int ktb = a.kt / kBlock;
-    const bool resident = a.kt >= a.k;
-    if (resident) {
-        stage_int_tile<R, WORDS>(a, lds, 0, a.k);
-        __syncthreads();
-    }
-    for (int64_t grp = blockIdx.x; grp < a.num_groups; grp += gridDim.x) {
-        const int64_t n0 = (grp * kWaves + wave) * MR;
-        double acc[MR][R];
+    const int kb0 = it.ti * ktb;
+    const int nbt = min(ktb, a.nb - kb0);
+    const int bl = it.u * 64 + lane;
+    if (bl >= nbt) return;
+    const float *lx = reinterpret_cast<const float *>(lds);
+    uint32_t q[8];
+    window_quants(win[0], window_selector(bl), q);
+    const double d = static_cast<double>(f16_bits_to_float(window_scale_bits(win[0], bl)));
 #pragma unroll
-        for (int m = 0; m < MR; ++m)
+    for (int r = 0; r < R; ++r) {
+        const float4 *px = reinterpret_cast<const float4 *>(lx + r * a.kt + bl * kBlock);
+        double p = 0.0;
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[m][r] = 0.0;
-
-        for (int kt0 = 0; kt0 < a.k; kt0 += a.kt) {
-            const int ktc = min(a.kt, a.k - kt0);
-            if (!resident) {
-                __syncthreads();
-                stage_int_tile<R, WORDS>(a, lds, kt0, ktc);
-                __syncthreads();
-            }
-            const int tbk = ktc / kBlock, kb0 = kt0 / kBlock;
-            for (int bl0 = 0; bl0 < tbk; bl0 += 64 * U) {
-                Window win[U][MR];
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-#pragma unroll
-                    for (int m = 0; m < MR; ++m) {
-                        const int bl = bl0 + 64 * u + lane;
-                        if (bl < tbk && n0 + m < a.n)
-                            load_window(a.w, (n0 + m) * a.nb + kb0 + bl, win[u][m]);
-                        else
-                            zero_window(win[u][m]);
-                    }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int bl = bl0 + 64 * u + lane;
-                    if (bl >= tbk) continue;
-                    uint32_t q[MR][8];
-                    double d[MR];
-#pragma unroll
-                    for (int m = 0; m < MR; ++m) {
-                        const int64_t g = (n0 + m) * a.nb + kb0 + bl;
-                        window_quants(win[u][m], window_selector(g), q[m]);
-                        d[m] = static_cast<double>(f16_bits_to_float(window_scale_bits(win[u][m], g)));
-                    }
-#pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        uint32_t h[8], l[8];
-                        const uint4 *ph = reinterpret_cast<const uint4 *>(lhi + r * a.kt + bl * kBlock);
-                        const uint4 h0 = ph[0], h1 = ph[1];
-                        h[0] = h0.x; h[1] = h0.y; h[2] = h0.z; h[3] = h0.w;
-                        h[4] = h1.x; h[5] = h1.y; h[6] = h1.z; h[7] = h1.w;
-                        if (WORDS == 2) {
-                            const uint4 *pl = reinterpret_cast<const uint4 *>(llo + r * a.kt + bl * kBlock);
-                            const uint4 l0 = pl[0], l1 = pl[1];
-                            l[0] = l0.x; l[1] = l0.y; l[2] = l0.z; l[3] = l0.w;
-                            l[4] = l1.x; l[5] = l1.y; l[6] = l1.z; l[7] = l1.w;
-                        }
-                        const double s = ls[r * ktb + bl];
-#pragma unroll
-                        for (int m = 0; m < MR; ++m) {
-                            int32_t t = dot32(q[m], h);
-                            if (WORDS == 2) t = t * 128 + dot32(q[m], l);
-                            acc[m][r] += (d[m] * s) * static_cast<double>(t);
-                        }
-                    }
-                }
-            }
+        for (int j = 0; j < 8; ++j) {
+            const float4 xv = px[j];
+            const uint32_t qw = q[j];
+            p = __builtin_fma(static_cast<double>(static_cast<int8_t>(qw)), static_cast<double>(xv.x), p);
+            p = __builtin_fma(static_cast<double>(static_cast<int8_t>(qw >> 8)), static_cast<double>(xv.y), p);
+            p = __builtin_fma(static_cast<double>(static_cast<int8_t>(qw >> 16)), static_cast<double>(xv.z), p);
+            p = __builtin_fma(static_cast<double>(static_cast<int8_t>(qw >> 24)), static_cast<double>(xv.w), p);
         }
-#pragma unroll
-        for (int m = 0; m < MR; ++m)
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const double tot = wave_sum(acc[m][r]);
-                const int64_t nn = n0 + m;
-                if (lane == ((m * R + r) & 63) && nn < a.n) {
-                    const int64_t o = static_cast<int64_t>(r) * a.n + nn;
-                    const double res = a.residual ? static_cast<double>(a.residual[o]) : 0.0;
-                    a.y[o] = static_cast<float>(tot + res);
-                }
-            }
+        acc[0][r] += d * p;
     }
 }
 
-// ------------------------------------------------------------------- f32 mode
+template <int R, int WORDS, int MR>
+__device__ __forceinline__ void compute_item(const GemvArgs &a, const uint8_t *lds, const Item &it, int lane,
+                                             const Window (&win)[MR], double (&acc)[MR][R]) {
+    if constexpr (WORDS == 0)
+        compute_f64_item<R, MR>(a, lds, it, lane, win, acc);
+    else
+        compute_int_item<R, WORDS, MR>(a, lds, it, lane, win, acc);
+}
 
-// LDS tile: x [R][kt] f32.  Every product q*x and every sum is f64.
-template <int R>
-__device__ __forceinline__ void stage_f32_tile(const GemvArgs &a, float *lds, int kt0, int ktc) {
-    const int vec_per_row = ktc / 4;
-    for (int i = threadIdx.x; i < R * vec_per_row; i += kThreads) {
-        const int r = i / vec_per_row, c = (i % vec_per_row) * 4;
-        *reinterpret_cast<float4 *>(lds + r * a.kt + c) =
-            *reinterpret_cast<const float4 *>(a.x + static_cast<int64_t>(r) * a.k + kt0 + c);
+template <int R, int WORDS>
+__device__ __forceinline__ void stage_tile(const GemvArgs &a, uint8_t *lds, int ti, int wave, int lane) {
+    if constexpr (WORDS == 0)
+        stage_f32<R>(a, lds, ti, wave, lane);
+    else
+        stage_int<R, WORDS>(a, lds, ti, wave, lane);
+}
+
+// Output element (r, row): the f64 total plus the residual in f64, rounded once.
+__device__ __forceinline__ void write_output(const GemvArgs &a, int r, int64_t row, double tot) {
+    const int64_t o = static_cast<int64_t>(r) * a.ldy + row;
+    const double res = a.residual ? static_cast<double>(a.residual[o]) : 0.0;
+    a.y[o] = static_cast<float>(tot + res);
+}
+
+__host__ __device__ inline size_t stack_bytes(int rows, int words, int kt) {
+    return words == 0 ? static_cast<size_t>(rows) * kt * 4
+                      : static_cast<size_t>(rows) * words * kt + static_cast<size_t>(rows) * (kt / kBlock) * 4;
+}
+
+// ------------------------------------------------------------ resident kernel
+
+// The whole matrix as one range-checked buffer (the launcher keeps it under
+// 2^31 bytes).  Offsets are byte offsets into it; kOob reads zeros.
+struct WeightStream {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t lane_part;  // this lane's window offset within a 64-block column: (lane*34) & ~3
+    uint32_t row_bytes;  // nb * 34
+};
+
+template <int MR>
+__device__ __forceinline__ void stream_item(const WeightStream &ws, uint32_t item_base, bool lane_ok,
+                                            Window (&win)[MR]) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        // item_base: byte offset of the item's first block in its group's first row,
+        // or kOob for a dead refill (then every offset below stays out of range)
+        const uint32_t off = lane_ok ? item_base + m * ws.row_bytes + ws.lane_part : kOob;
+        const u32x4 d0 = __builtin_amdgcn_raw_buffer_load_b128(ws.rsrc, off, 0, kLoadPolicy);
+        const u32x4 d1 = __builtin_amdgcn_raw_buffer_load_b128(ws.rsrc, off + 16, 0, kLoadPolicy);
+        const uint32_t d2 = __builtin_amdgcn_raw_buffer_load_b32(ws.rsrc, off + 32, 0, kLoadPolicy);
+        win[m].d[0] = d0.x; win[m].d[1] = d0.y; win[m].d[2] = d0.z; win[m].d[3] = d0.w;
+        win[m].d[4] = d1.x; win[m].d[5] = d1.y; win[m].d[6] = d1.z; win[m].d[7] = d1.w;
+        win[m].d[8] = d2;
     }
 }
 
-template <int R, int U>
-__global__ __launch_bounds__(kThreads) void gemv_f64_kernel(GemvArgs a) {
-    extern __shared__ __align__(16) uint8_t lds_raw[];
-    float *lx = reinterpret_cast<float *>(lds_raw);
+// Position of a wave in its item sequence: group gi (the wave's gi-th row group)
+// and 64-block column u.  Advanced one item at a time.
+struct Cursor {
+    int gi;
+    int u;
+    __device__ __forceinline__ void next(int ub) {
+        if (++u == ub) {
+            u = 0;
+            ++gi;
+        }
+    }
+};
+
+// WORDS = 1 or 2 (integer modes) or 0 (f32 mode).
+template <int R, int WORDS, int MR, int P>
+__global__ __launch_bounds__(kThreads) void gemv_resident_kernel(GemvArgs a) {
+    extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const bool resident = a.kt >= a.k;
-    if (resident) {
-        stage_f32_tile<R>(a, lx, 0, a.k);
-        __syncthreads();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+    const int G = gw < a.num_groups ? static_cast<int>((a.num_groups - gw + stride - 1) / stride) : 0;
+    const int ub = a.ub;
+    const int T = G * ub;
+    // per-row totals parked until the pipeline has drained: [group][m][r] f64
+    const size_t totals_at = (stack_bytes(R, WORDS, a.kt) + 15) & ~size_t(15);
+    double *totals = reinterpret_cast<double *>(lds + totals_at) + wave * kOutPerWave;
+
+    WeightStream ws;
+    ws.row_bytes = static_cast<uint32_t>(a.nb) * kBlockBytes;
+    ws.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.w), 0,
+                                                static_cast<int>(static_cast<uint32_t>(a.n) * ws.row_bytes),
+                                                kBufferDword3);
+    ws.lane_part = static_cast<uint32_t>(lane * kBlockBytes) & ~3u;
+    const uint32_t group_bytes = ws.row_bytes * MR;
+    const uint32_t grid_group_bytes = static_cast<uint32_t>(stride) * group_bytes;
+    const uint32_t first_group_bytes = static_cast<uint32_t>(gw) * group_bytes;
+    // byte offset of item (gi, u) in the matrix, or kOob past the wave's items
+    auto item_base = [&](const Cursor &c) -> uint32_t {
+        return c.gi < G ? first_group_bytes + c.gi * grid_group_bytes + c.u * (64 * kBlockBytes) : kOob;
+    };
+    auto lane_ok = [&](const Cursor &c) { return c.u * 64 + lane < a.nb; };
+
+    // Prologue: stage the stack (L2), then put the first P items of weights (HBM)
+    // in flight, and barrier once the stack has landed.
+    stage_tile<R, WORDS>(a, lds, 0, wave, lane);
+    Window ring[P][MR];
+    Cursor ahead{0, 0};
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        stream_item<MR>(ws, item_base(ahead), lane_ok(ahead), ring[p]);
+        ahead.next(ub);
     }
-    for (int64_t grp = blockIdx.x; grp < a.num_groups; grp += gridDim.x) {
-        const int64_t nn = grp * kWaves + wave;  // one output row per wave
-        double acc[R];
+    staged_barrier<P * MR * kLoadsPerWindow>();
+
+    double acc[MR][R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = 0.0;
-        for (int kt0 = 0; kt0 < a.k; kt0 += a.kt) {
-            const int ktc = min(a.kt, a.k - kt0);
-            if (!resident) {
-                __syncthreads();
-                stage_f32_tile<R>(a, lx, kt0, ktc);
-                __syncthreads();
-            }
-            const int tbk = ktc / kBlock, kb0 = kt0 / kBlock;
-            for (int bl0 = 0; bl0 < tbk; bl0 += 64 * U) {
-                Window win[U];
+    for (int m = 0; m < MR; ++m)
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int bl = bl0 + 64 * u + lane;
-                    if (bl < tbk && nn < a.n)
-                        load_window(a.w, nn * a.nb + kb0 + bl, win[u]);
-                    else
-                        zero_window(win[u]);
-                }
+        for (int r = 0; r < R; ++r) acc[m][r] = 0.0;
+
+    Cursor cur{0, 0};
+    for (int t0 = 0; t0 < T; t0 += P) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int bl = bl0 + 64 * u + lane;
-                    if (bl >= tbk) continue;
-                    const int64_t g = nn * a.nb + kb0 + bl;
-                    uint32_t q[8];
-                    window_quants(win[u], window_selector(g), q);
-                    const double d = static_cast<double>(f16_bits_to_float(window_scale_bits(win[u], g)));
+        for (int p = 0; p < P; ++p) {
+            const Item it{gw + static_cast<int64_t>(cur.gi) * stride, 0, cur.u};
+            compute_item<R, WORDS, MR>(a, lds, it, lane, ring[p], acc);
+            stream_item<MR>(ws, item_base(ahead), lane_ok(ahead), ring[p]);
+            ahead.next(ub);
+            if (cur.gi < G && cur.u == ub - 1) {
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
-                        const float4 *px = reinterpret_cast<const float4 *>(lx + r * a.kt + bl * kBlock);
-                        double p = 0.0;
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const float4 xv = px[j];
-                            const uint32_t qw = q[j];
-                            p = __builtin_fma(static_cast<double>(static_cast<int8_t>(qw)), static_cast<double>(xv.x), p);
-                            p = __builtin_fma(static_cast<double>(static_cast<int8_t>(qw >> 8)), static_cast<double>(xv.y), p);
-                            p = __builtin_fma(static_cast<double>(static_cast<int8_t>(qw >> 16)), static_cast<double>(xv.z), p);
-                            p = __builtin_fma(static_cast<double>(static_cast<int8_t>(qw >> 24)), static_cast<double>(xv.w), p);
-                        }
-                        acc[r] += d * p;
+                        const double tot = wave_sum(acc[m][r]);
+                        acc[m][r] = 0.0;
+                        if (lane == 0) totals[(cur.gi * MR + m) * R + r] = tot;
                     }
-                }
             }
+            cur.next(ub);
         }
+    }
+    // Epilogue: scale (1/128 in two-word mode, exact), residual, one rounding.
+    const double post = WORDS == 2 ? 1.0 / 128.0 : 1.0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int i = lane; i < G * MR * R; i += 64) {
+        const int gi = i / (MR * R), m = (i / R) % MR, r = i % R;
+        const int64_t row = (gw + static_cast<int64_t>(gi) * stride) * MR + m;
+        if (row < a.n) write_output(a, r, row, totals[i] * post);
+    }
+}
+
+// --------------------------------------------------------------- tiled kernel
+
+// The stack is staged one column tile at a time; each wave owns one row group and
+// keeps its (at most kTiledMaxUb) items of the tile in registers.
+template <int R, int WORDS, int MR>
+__global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(GemvArgs a) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t grp = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+    double acc[MR][R];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[m][r] = 0.0;
+    for (int ti = 0; ti < a.ntiles; ++ti) {
+        if (ti > 0) __syncthreads();  // every wave is done with the previous tile
+        stage_tile<R, WORDS>(a, lds, ti, wave, lane);
+        Window win[kTiledMaxUb][MR];
+#pragma unroll
+        for (int u = 0; u < kTiledMaxUb; ++u)
+            issue_item<MR>(a, Item{grp, ti, u}, u < a.ub && grp < a.num_groups, lane, win[u]);
+        staged_barrier<kTiledMaxUb * MR * kLoadsPerWindow>();
+#pragma unroll
+        for (int u = 0; u < kTiledMaxUb; ++u)
+            if (u < a.ub) compute_item<R, WORDS, MR>(a, lds, Item{grp, ti, u}, lane, win[u], acc);
+    }
+    const double post = WORDS == 2 ? 1.0 / 128.0 : 1.0;
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const double tot = wave_sum(acc[r]);
-            if (lane == r && nn < a.n) {
-                const int64_t o = static_cast<int64_t>(r) * a.n + nn;
-                const double res = a.residual ? static_cast<double>(a.residual[o]) : 0.0;
-                a.y[o] = static_cast<float>(tot + res);
-            }
+            const double tot = wave_sum(acc[m][r]) * post;
+            const int64_t row = grp * MR + m;
+            if (lane == ((m * R + r) & 63) && row < a.n) write_output(a, r, row, tot);
         }
-    }
 }
 
 // ------------------------------------------------------------------- launchers
 
-constexpr int kLdsBudget = 64 * 1024;  // per workgroup; leaves room for 2 workgroups a CU
-
-int round_down_256(int64_t v) { return static_cast<int>((v / 256) * 256); }
-
-template <int R, int WORDS, int MR, int U>
-hipError_t run_int(GemvArgs a, hipStream_t stream) {
-    const int64_t per_col_num = static_cast<int64_t>(R) * WORDS * 32 + R * 8;  // bytes per 32 columns
-    int kt = round_down_256(static_cast<int64_t>(kLdsBudget) * 32 / per_col_num);
-    if (kt >= a.k) kt = a.k;
-    a.kt = kt;
-    const size_t lds = static_cast<size_t>(R) * WORDS * kt + static_cast<size_t>(R) * (kt / kBlock) * 8;
-    a.num_groups = (a.n + kWaves * MR - 1) / (kWaves * MR);
-    const DeviceInfo dev = device_info();
-    int64_t grid = a.num_groups;
-    if (kt >= a.k) {
-        const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (160 * 1024) / std::max<size_t>(lds, 1)));
-        grid = std::min<int64_t>(grid, per_cu * dev.cus);
-    }
-    gemv_int_kernel<R, WORDS, MR, U><<<dim3(static_cast<unsigned>(grid)), kThreads, lds, stream>>>(a);
-    return hipGetLastError();
+// Tile width (columns, a multiple of 64): the whole k when the staged stack fits
+// the LDS budget, else k split into equal tiles that fit and hold at most
+// kTiledMaxUb 64-block columns.
+int tile_columns(int k, int rows, int words) {
+    const int64_t per64 = static_cast<int64_t>(stack_bytes(rows, words, 64));
+    int64_t kt_max = std::max<int64_t>(64, (kLdsBudget / per64) * 64);
+    if (kt_max >= k) return k;
+    kt_max = std::min<int64_t>(kt_max, static_cast<int64_t>(kTiledMaxUb) * 64 * kBlock);
+    const int64_t ntiles = (k + kt_max - 1) / kt_max;
+    return static_cast<int>(((k + ntiles - 1) / ntiles + 63) / 64 * 64);
 }
 
-template <int R, int U>
-hipError_t run_f64(GemvArgs a, hipStream_t stream) {
-    int kt = round_down_256(static_cast<int64_t>(kLdsBudget) / (4 * R));
-    if (kt >= a.k) kt = a.k;
-    a.kt = kt;
-    const size_t lds = static_cast<size_t>(R) * kt * 4;
-    a.num_groups = (a.n + kWaves - 1) / kWaves;
-    const DeviceInfo dev = device_info();
-    int64_t grid = a.num_groups;
-    if (kt >= a.k) {
-        const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (160 * 1024) / std::max<size_t>(lds, 1)));
-        grid = std::min<int64_t>(grid, per_cu * dev.cus);
+constexpr int kWavesPerCu = 8;
+
+template <int R, int WORDS, int MR, int P>
+hipError_t run(GemvArgs a, hipStream_t stream) {
+    a.kt = tile_columns(a.k, R, WORDS);
+    a.ntiles = (a.k + a.kt - 1) / a.kt;
+    a.ub = (a.kt / kBlock + 63) / 64;
+    a.num_groups = (a.n + MR - 1) / MR;
+    const size_t stack = stack_bytes(R, WORDS, a.kt);
+    const int64_t row_bytes = static_cast<int64_t>(a.nb) * kBlockBytes;
+    if (a.ntiles == 1 && a.n * row_bytes > kMaxStreamBytes) {
+        // The resident kernel addresses the matrix as one buffer: run it on row
+        // slices of at most kMaxStreamBytes.
+        const int64_t slice = std::max<int64_t>(MR, (kMaxStreamBytes / row_bytes) / MR * MR);
+        for (int64_t r0 = 0; r0 < a.n; r0 += slice) {
+            GemvArgs s = a;
+            s.w = a.w + r0 * row_bytes;
+            s.n = std::min(slice, a.n - r0);
+            s.y = a.y + r0;
+            s.residual = a.residual ? a.residual + r0 : nullptr;
+            if (hipError_t e = run<R, WORDS, MR, P>(s, stream); e != hipSuccess) return e;
+        }
+        return hipSuccess;
     }
-    gemv_f64_kernel<R, U><<<dim3(static_cast<unsigned>(grid)), kThreads, lds, stream>>>(a);
+    if (a.ntiles == 1) {
+        const DeviceInfo dev = device_info();
+        // enough waves to fill the chip, and enough that none parks more than
+        // kOutPerWave totals
+        const int64_t groups_cap = kOutPerWave / (MR * R);
+        const int64_t min_waves = (a.num_groups + groups_cap - 1) / groups_cap;
+        int64_t waves = std::min<int64_t>(a.num_groups, static_cast<int64_t>(dev.cus) * kWavesPerCu);
+        waves = std::max<int64_t>(waves, min_waves);
+        const int64_t grid = (waves + kWaves - 1) / kWaves;
+        const size_t lds = ((stack + 15) & ~size_t(15)) + static_cast<size_t>(kWaves) * kOutPerWave * 8;
+        gemv_resident_kernel<R, WORDS, MR, P><<<dim3(static_cast<unsigned>(grid)), kThreads, lds, stream>>>(a);
+    } else {
+        const int64_t grid = (a.num_groups + kWaves - 1) / kWaves;
+        gemv_tiled_kernel<R, WORDS, MR><<<dim3(static_cast<unsigned>(grid)), kThreads, stack, stream>>>(a);
+    }
     return hipGetLastError();
 }
 
 template <int WORDS>
 hipError_t dispatch_int(int rows, const GemvArgs &a, hipStream_t s) {
     switch (rows) {
-        case 1: return run_int<1, WORDS, 1, 4>(a, s);
-        case 2: return run_int<2, WORDS, 2, 2>(a, s);
-        case 3: return run_int<3, WORDS, 2, 2>(a, s);
-        case 4: return run_int<4, WORDS, 2, 1>(a, s);
-        case 5: return run_int<5, WORDS, 2, 1>(a, s);
-        case 6: return run_int<6, WORDS, 2, 1>(a, s);
-        case 7: return run_int<7, WORDS, 2, 1>(a, s);
-        default: return run_int<8, WORDS, 2, 1>(a, s);
+        case 1: return run<1, WORDS, 1, 2>(a, s);
+        case 2: return run<2, WORDS, 2, 4>(a, s);
+        case 3: return run<3, WORDS, 2, 4>(a, s);
+        case 4: return run<4, WORDS, 2, 4>(a, s);
+        case 5: return run<5, WORDS, 2, 2>(a, s);
+        case 6: return run<6, WORDS, 2, 2>(a, s);
+        case 7: return run<7, WORDS, 2, 2>(a, s);
+        default: return run<8, WORDS, 2, 2>(a, s);
     }
 }
 
 hipError_t dispatch_f64(int rows, const GemvArgs &a, hipStream_t s) {
     switch (rows) {
-        case 1: return run_f64<1, 2>(a, s);
-        case 2: return run_f64<2, 2>(a, s);
-        case 3: return run_f64<3, 1>(a, s);
-        case 4: return run_f64<4, 1>(a, s);
-        case 5: return run_f64<5, 1>(a, s);
-        case 6: return run_f64<6, 1>(a, s);
-        case 7: return run_f64<7, 1>(a, s);
-        default: return run_f64<8, 1>(a, s);
+        case 1: return run<1, 0, 1, 2>(a, s);
+        case 2: return run<2, 0, 1, 4>(a, s);
+        case 3: return run<3, 0, 1, 4>(a, s);
+        case 4: return run<4, 0, 1, 4>(a, s);
+        case 5: return run<5, 0, 1, 2>(a, s);
+        case 6: return run<6, 0, 1, 2>(a, s);
+        case 7: return run<7, 0, 1, 2>(a, s);
+        default: return run<8, 0, 1, 2>(a, s);
     }
 }
 
@@ -324,6 +536,7 @@ hipError_t launch_gemv(int mode, const uint8_t *w, int64_t n, int64_t k, int row
     a.residual = residual;
     a.y = y;
     a.n = n;
+    a.ldy = n;
     a.k = static_cast<int>(k);
     a.nb = static_cast<int>(k / kBlock);
     if (mode == 0) return dispatch_f64(rows, a, stream);
