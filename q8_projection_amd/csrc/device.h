@@ -70,6 +70,31 @@ __device__ __forceinline__ int32_t dot32(const uint32_t (&q)[8], const uint32_t 
     return acc;
 }
 
+// Buffer loads here address ranges under 2^31 bytes.  An offset with bit 31 set
+// is past every range, so the load returns zeros and touches no memory.
+// oob_bit(ok) is 0 for an in-range lane and that bit otherwise: OR-ing it in is
+// plain arithmetic, so the compiler has no select to turn into a branch
+// around the load.
+__device__ __forceinline__ uint32_t oob_bit(bool ok) { return static_cast<uint32_t>(!ok) << 31; }
+
+// Order this wave's LDS writes before its later LDS reads, for data exchanged
+// between lanes of the wave (no instruction is emitted: LDS operations of one
+// wave are already in order; this stops the compiler from reusing values it
+// loaded before the exchange).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Workgroup barrier after this wave's LDS writes have already been waited for
+// by the caller (an explicit s_waitcnt): the acquire fence keeps later LDS
+// reads from being moved above the barrier or served from earlier loads.
+__device__ __forceinline__ void workgroup_barrier_acquire_lds() {
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // One DPP move of a double (each 32-bit half moved with the same control).
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {

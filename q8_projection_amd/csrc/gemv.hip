@@ -104,14 +104,15 @@ __device__ __forceinline__ void dma_rows4(float *dst, int dst_stride, const floa
 // then barrier.  The direct-to-LDS copies of a tile are issued before the N
 // weight loads that follow them, and vmcnt retires in order, so after the wait
 // this wave's copies have landed while its weight loads stay in flight; after
-// the barrier every wave's copies have.  A bare s_barrier is used: the fences of
-// __syncthreads would make the compiler wait for the weight loads too.
+// the barrier every wave's copies have.  The explicit wait is the release; a
+// release fence would make the compiler wait for the weight loads too (the
+// direct-to-LDS copies count as LDS writes under vmcnt).
 template <int N>
 __device__ __forceinline__ void staged_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt is six bits");
     // s_waitcnt fields (gfx9): vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]
     __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | 0x70 | 0xf00);
-    __builtin_amdgcn_s_barrier();
+    workgroup_barrier_acquire_lds();
 }
 
 // Integer modes.  LDS: hi [R][kt] bytes, lo [R][kt] bytes (two-word), scales [R][kt/32] f32.
@@ -162,7 +163,7 @@ __device__ __forceinline__ void issue_item(const GemvArgs &a, const Item &it, bo
     for (int m = 0; m < MR; ++m) {
         const bool ok = bl < nbt && m < rows_here;
         const uint32_t off =
-            ok ? static_cast<uint32_t>(window_offset(static_cast<int64_t>(m) * a.nb + kb0 + bl)) : kOob;
+            static_cast<uint32_t>(window_offset(static_cast<int64_t>(m) * a.nb + kb0 + bl)) | oob_bit(ok);
         const u32x4 d0 = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kLoadPolicy);
         const u32x4 d1 = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 16, 0, kLoadPolicy);
         const uint32_t d2 = __builtin_amdgcn_raw_buffer_load_b32(rsrc, off + 32, 0, kLoadPolicy);
@@ -297,7 +298,7 @@ __device__ __forceinline__ void stream_item(const WeightStream &ws, uint32_t ite
     for (int m = 0; m < MR; ++m) {
         // item_base: byte offset of the item's first block in its group's first row,
         // or kOob for a dead refill (then every offset below stays out of range)
-        const uint32_t off = lane_ok ? item_base + m * ws.row_bytes + ws.lane_part : kOob;
+        const uint32_t off = (item_base + m * ws.row_bytes + ws.lane_part) | oob_bit(lane_ok);
         const u32x4 d0 = __builtin_amdgcn_raw_buffer_load_b128(ws.rsrc, off, 0, kLoadPolicy);
         const u32x4 d1 = __builtin_amdgcn_raw_buffer_load_b128(ws.rsrc, off + 16, 0, kLoadPolicy);
         const uint32_t d2 = __builtin_amdgcn_raw_buffer_load_b32(ws.rsrc, off + 32, 0, kLoadPolicy);
@@ -391,9 +392,7 @@ __global__ __launch_bounds__(kThreads) void gemv_resident_kernel(GemvArgs a) {
     }
     // Epilogue: scale (1/128 in two-word mode, exact), residual, one rounding.
     const double post = WORDS == 2 ? 1.0 / 128.0 : 1.0;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_sync();  // lane 0 parked the totals the whole wave reads now
     for (int i = lane; i < G * MR * R; i += 64) {
         const int gi = i / (MR * R), m = (i / R) % MR, r = i % R;
         const int64_t row = (gw + static_cast<int64_t>(gi) * stride) * MR + m;
