@@ -37,40 +37,37 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "Q8_0 projection effective weight GB/s and % HBM peak at rows=1/8/64"
-COUNTERS = os.path.join(ROOT, "profiles", "lm_head_gemv_counters.txt")
-KERNEL_SOURCES = ["q8_projection_amd/csrc/gemv.hip", "q8_projection_amd/csrc/device.h"]
+PROFILES = os.path.join(ROOT, "profiles")
 
 
-def step_calls():
-    from synth import workloads as wl
-    by_name = {c.name: c for c in wl.all_calls()}
-    return [by_name["down_i8x2"], by_name["batch8"], by_name["batch8_down_res"], by_name["prefill64"],
-            by_name["lm_head"]]
-
-
-def kernel_hash() -> str:
+def kernel_hash(sources) -> str:
+    """First 16 hex digits of the SHA-256 over the named kernel sources, in order."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None if it is missing or was taken on other kernel sources."""
+def stored_traffic(call_name: str):
+    """HBM bytes per launch of a call from its committed counter summary
+    (profiles/<call>_*counters.txt), or None if there is none or it was taken on
+    kernel sources other than the current ones."""
     try:
-        fields = {}
-        with open(COUNTERS) as f:
-            for line in f:
-                if "=" in line and not line.lstrip().startswith("#"):
-                    k, v = line.split("=", 1)
-                    fields[k.strip()] = v.strip()
-        if fields.get("kernel_sources_sha256_16") != kernel_hash():
-            return None
-        return float(fields["hbm_bytes_per_launch"])
+        names = [f for f in os.listdir(PROFILES) if f.startswith(call_name + "_") and f.endswith("counters.txt")]
+        for fname in names:
+            fields = {}
+            with open(os.path.join(PROFILES, fname)) as f:
+                for line in f:
+                    if "=" in line and not line.lstrip().startswith("#"):
+                        k, v = line.split("=", 1)
+                        fields[k.strip()] = v.strip()
+            sources = fields.get("kernel_sources", "").split()
+            if sources and fields.get("kernel_sources_sha256_16") == kernel_hash(sources):
+                return float(fields["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
-        return None
+        pass
+    return None
 
 
 class Prepared:
@@ -197,6 +194,9 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None, help="run only the named call eagerly (for profilers)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="with --only: also run torch's device copy of this many MiB, 4 times (the "
+                         "known-size reference for HBM byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (a projection's share of a "
@@ -221,7 +221,18 @@ def main(argv=None):
         for i in range(args.warmup + args.steps):
             p.project(i % p.copies)
         torch.cuda.synchronize()
-        print(json.dumps({"only": args.only, "launches": args.warmup + args.steps}))
+        copied = 0
+        if args.calib_copy_mib:
+            n = args.calib_copy_mib << 20
+            src = torch.ones(n, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            for _ in range(4):
+                dst.copy_(src)
+                copied += n
+            torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "launches": args.warmup + args.steps,
+                          "weight_bytes_per_launch": p.call.weight_bytes, "calib_copy_bytes_each": copied // 4}))
         return 0
 
     def step(copy):
@@ -282,7 +293,7 @@ def main(argv=None):
     dom_name = max(per_call, key=lambda n: per_call[n]["project_us"])
     dom = per_call[dom_name]
     achieved = dom["weight_bytes"] / (dom["project_us"] * 1e-6) / 1e9
-    traffic = stored_traffic() if dom_name == "lm_head" else None
+    traffic = stored_traffic(dom_name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": f"{dom_name}: rows={dom['rows']} {dom['n']}x{dom['k']} {dom['mode']}",
