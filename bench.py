@@ -40,6 +40,13 @@ METRIC = "Q8_0 projection effective weight GB/s and % HBM peak at rows=1/8/64"
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+def step_calls():
+    from synth import workloads as wl
+    by_name = {c.name: c for c in wl.all_calls()}
+    return [by_name["down_i8x2"], by_name["batch8"], by_name["batch8_down_res"], by_name["prefill64"],
+            by_name["lm_head"]]
+
+
 def kernel_hash(sources) -> str:
     """First 16 hex digits of the SHA-256 over the named kernel sources, in order."""
     h = hashlib.sha256()

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libq8proj.so")
-SOURCES = ["abi.cpp", "quantize.hip", "gemv.hip", "mfma.hip", "sums.hip"]
+SOURCES = ["abi.cpp", "quantize.hip", "gemv.hip", "mma.hip", "sums.hip"]
 ARCH = "gfx950"
 
 # Packed f32 VALU ops are kept out of the device code; the host pass warns that

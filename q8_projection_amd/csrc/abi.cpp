@@ -152,8 +152,8 @@ q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t 
         const float *sres = residual ? residual + r0 * n : nullptr;
         float *sy = y + r0 * n;
         hipError_t e;
-        if (r > 8 && q8::mfma_supports(mode, r)) {
-            e = q8::launch_mfma(mode, wb, n, k, r, shi, slo, ssc, sres, sy, st);
+        if (q8::mma_supports(mode, n, k, r, wb, shi, slo, ssc)) {
+            e = q8::launch_mma(mode, wb, n, k, r, shi, slo, ssc, sres, sy, n, st);
         } else {
             // the GEMV family, 8 rows at a time
             e = hipSuccess;

@@ -25,12 +25,15 @@ hipError_t launch_gemv(int mode, const uint8_t *w, int64_t n, int64_t k, int row
                        const int8_t *lo, const float *scale, const float *x, const float *residual,
                        float *y, hipStream_t stream);
 
-// Projection of 9..64 rows with the int8 MFMA kernel (integer modes).
-hipError_t launch_mfma(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
-                       const int8_t *lo, const float *scale, const float *residual, float *y,
-                       hipStream_t stream);
-// Whether launch_mfma serves (mode, rows).
-bool mfma_supports(int mode, int rows);
+// Projection of 2..64 rows with the LDS-staged int8 MFMA kernel (integer
+// modes).  y and residual have row stride ldy.
+hipError_t launch_mma(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
+                      const int8_t *lo, const float *scale, const float *residual, float *y, int64_t ldy,
+                      hipStream_t stream);
+// Whether launch_mma serves this call: integer mode, 2..64 rows, k a multiple
+// of 256, weights under 1 GiB, and weights, words and scales 16-byte aligned.
+bool mma_supports(int mode, int64_t n, int64_t k, int rows, const void *w, const void *hi, const void *lo,
+                  const void *scale);
 
 hipError_t launch_block_sums(int words, const uint8_t *w, int64_t n, int64_t k, int64_t rows,
                              const int8_t *hi, const int8_t *lo, int32_t *sums, hipStream_t stream);

@@ -1,0 +1,31 @@
+"""bench.py's host logic (no GPU): the step's calls, the one-GPU guard and the
+counter-summary lookup."""
+import os
+
+import bench
+
+
+def test_step_calls_are_the_measured_workloads():
+    names = [c.name for c in bench.step_calls()]
+    assert names == ["down_i8x2", "batch8", "batch8_down_res", "prefill64", "lm_head"]
+    rows = sorted({c.rows for c in bench.step_calls()})
+    assert rows == [1, 8, 64]
+
+
+def test_more_than_one_gpu_is_refused():
+    assert bench.main(["--gpus", "2"]) == 2
+
+
+def test_counter_summary_is_keyed_on_its_sources(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    h = bench.kernel_hash(["k.hip"])
+    (tmp_path / "demo_counters.txt").write_text(
+        f"# comment = ignored\nkernel_sources = k.hip\nkernel_sources_sha256_16 = {h}\nhbm_bytes_per_launch = 1234\n")
+    assert bench.stored_traffic("demo") == 1234.0
+    assert bench.stored_traffic("other") is None
+    src.write_text("kernel v2")
+    assert bench.stored_traffic("demo") is None
+    assert os.path.exists(tmp_path / "demo_counters.txt")

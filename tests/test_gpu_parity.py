@@ -188,7 +188,8 @@ def test_block_sums_bitwise(mode, n, k, rows):
 @pytest.mark.parametrize("mode", ["f32", "i8", "i8x2"])
 @pytest.mark.parametrize("n,k,rows", [(1, 64, 1), (3, 192, 2), (7, 2112, 3), (13, 4160, 5), (37, 320, 8),
                                       (29, 1024, 9), (17, 512, 12), (11, 256, 64), (5, 128, 65),
-                                      (130, 4096, 7)])
+                                      (130, 4096, 7), (1000, 1024, 2), (1000, 512, 17), (333, 768, 33),
+                                      (20000, 256, 6), (64, 2048, 48), (257, 256, 63)])
 def test_ragged_shapes(mode, n, k, rows):
     say("ragged", mode, n, k, rows)
     w = synth.weights(n, k, seed=200 + n, outlier_frac=0.1)
@@ -202,26 +203,41 @@ def test_ragged_shapes(mode, n, k, rows):
 
 
 def test_stack_rows_equal_single_rows():
-    """Within the GEMV family a stacked row gives the same bits as that row alone
-    (same block order, same reductions)."""
+    """A row's result does not depend on the rest of its stack.  f32 mode (the
+    GEMV family at every stack height): a stacked row equals that row alone.
+    Integer modes (the MFMA family serves 2..64 rows, with one summation order
+    per output whatever the stack): a row of an 8-row stack equals the same row
+    in a 2-row and in a 64-row stack.  Rows of a stack are within the gate of
+    the same row projected alone by the GEMV (different summation order)."""
     n, k = 515, 4096
     say("stack vs single rows", n, k)
     w = synth.weights(n, k, seed=501)
-    x = synth.activations(8, k, seed=502)
-    wd = to_dev(oracle.quantize_weights(w))
-    for mode in ("i8", "i8x2", "f32"):
-        xd = to_dev(x)
-        if mode == "f32":
-            ys = q8.matmul_rows(mode, wd, n, k, x=xd)
-            singles = [q8.matvec(mode, wd, n, k, x=xd[r]) for r in range(8)]
-        else:
-            hi, lo, sc = q8.quantize_act(mode, xd)
-            ys = q8.matmul_rows(mode, wd, n, k, hi=hi, lo=lo, scale=sc)
-            singles = [q8.matvec(mode, wd, n, k, hi=hi[r], lo=None if lo is None else lo[r], scale=sc[r])
-                       for r in range(8)]
+    x64 = synth.activations(64, k, seed=502)
+    blocks = oracle.quantize_weights(w)
+    wd = to_dev(blocks)
+    xd = to_dev(x64[:8])
+    ys = q8.matmul_rows("f32", wd, n, k, x=xd)
+    singles = [q8.matvec("f32", wd, n, k, x=xd[r]) for r in range(8)]
+    torch.cuda.synchronize()
+    for r in range(8):
+        assert torch.equal(ys[r], singles[r]), ("f32", r)
+    for mode in ("i8", "i8x2"):
+        hi, lo, sc = q8.quantize_act(mode, to_dev(x64))
+        ys64 = q8.matmul_rows(mode, wd, n, k, hi=hi, lo=lo, scale=sc)
+        ys8 = q8.matmul_rows(mode, wd, n, k, hi=hi[:8], lo=None if lo is None else lo[:8], scale=sc[:8])
+        for r0 in range(0, 8, 2):
+            ys2 = q8.matmul_rows(mode, wd, n, k, hi=hi[r0:r0 + 2], lo=None if lo is None else lo[r0:r0 + 2],
+                                 scale=sc[r0:r0 + 2])
+            torch.cuda.synchronize()
+            assert torch.equal(ys8[r0:r0 + 2], ys2), (mode, r0)
         torch.cuda.synchronize()
-        for r in range(8):
-            assert torch.equal(ys[r], singles[r]), (mode, r)
+        assert torch.equal(ys64[:8], ys8), mode
+        ohi, olo, osc = oracle.quantize_act(mode, x64[:8])
+        r, a = oracle.project(mode, blocks, n, k, 8, hi=ohi, lo=olo, scale=osc)
+        gate(ys8.cpu().numpy(), r, a, f"stack {mode}")
+        one = q8.matvec(mode, wd, n, k, hi=hi[3], lo=None if lo is None else lo[3], scale=sc[3])
+        torch.cuda.synchronize()
+        gate(one.cpu().numpy(), r[3], a[3], f"single {mode}")
 
 
 def test_inplace_residual_and_adjacent_buffers():
@@ -241,9 +257,9 @@ def test_inplace_residual_and_adjacent_buffers():
     assert torch.equal(inplace, y_sep)
 
 
-def test_outputs_stay_in_bounds():
-    """Canary words around every output are left untouched."""
-    n, k, rows = 333, 1088, 6
+@pytest.mark.parametrize("n,k,rows", [(333, 1088, 6), (333, 1024, 6), (333, 1024, 40)])
+def test_outputs_stay_in_bounds(n, k, rows):
+    """Canary words around every output and quantized input are left untouched."""
     say("canaries", n, k, rows)
     w = synth.weights(n, k, seed=701)
     x = synth.activations(rows, k, seed=702)
