@@ -69,10 +69,22 @@ struct GemvArgs {
 // (global_load_lds_dwordx4 / _dword): the data never passes through VGPRs.  One
 // wave-wide instruction moves one chunk (64 lanes x 16 or 4 bytes) to a
 // wave-uniform LDS address; chunks are dealt round-robin to the workgroup's
-// waves.  Callers wait for the copies (vmcnt) and then barrier.
+// waves.  Callers wait for the copies (vmcnt) and then barrier.  The copies are
+// inline assembly: the compiler does not track them, so it never adds waits for
+// them on its own (every wait on them is the caller's explicit one), and the
+// weight stream behind them is not drained before each LDS read.
 
-typedef __attribute__((address_space(1))) const void *gptr_t;
 typedef __attribute__((address_space(3))) void *lptr_t;
+
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((uintptr_t)(lptr_t)p));
+}
+__device__ __forceinline__ void lds_copy16(const void *src, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_copy4(const void *src, uint32_t lds) {
+    asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
 
 // rows x bytes (bytes a multiple of 16) from src (row stride src_stride) to LDS
 // dst (row stride dst_stride), 16 bytes per lane.
@@ -81,9 +93,8 @@ __device__ __forceinline__ void dma_rows16(uint8_t *dst, int dst_stride, const u
     const int per_row = (bytes + 1023) / 1024;
     for (int c = wave; c < rows * per_row; c += kWaves) {
         const int r = c / per_row, off = (c - r * per_row) * 1024;
-        if (off + lane * 16 < bytes)
-            __builtin_amdgcn_global_load_lds((gptr_t)(src + r * src_stride + off + lane * 16),
-                                             (lptr_t)(dst + r * dst_stride + off), 16, 0, 0);
+        const uint32_t to = lds_address(dst + r * dst_stride + off);
+        if (off + lane * 16 < bytes) lds_copy16(src + r * src_stride + off + lane * 16, to);
     }
 }
 
@@ -94,9 +105,8 @@ __device__ __forceinline__ void dma_rows4(float *dst, int dst_stride, const floa
     const int per_row = (count + 63) / 64;
     for (int c = wave; c < rows * per_row; c += kWaves) {
         const int r = c / per_row, off = (c - r * per_row) * 64;
-        if (off + lane < count)
-            __builtin_amdgcn_global_load_lds((gptr_t)(src + r * src_stride + off + lane),
-                                             (lptr_t)(dst + r * dst_stride + off), 4, 0, 0);
+        const uint32_t to = lds_address(dst + r * dst_stride + off);
+        if (off + lane < count) lds_copy4(src + r * src_stride + off + lane, to);
     }
 }
 
@@ -104,9 +114,7 @@ __device__ __forceinline__ void dma_rows4(float *dst, int dst_stride, const floa
 // then barrier.  The direct-to-LDS copies of a tile are issued before the N
 // weight loads that follow them, and vmcnt retires in order, so after the wait
 // this wave's copies have landed while its weight loads stay in flight; after
-// the barrier every wave's copies have.  The explicit wait is the release; a
-// release fence would make the compiler wait for the weight loads too (the
-// direct-to-LDS copies count as LDS writes under vmcnt).
+// the barrier every wave's copies have.  The explicit wait is the release.
 template <int N>
 __device__ __forceinline__ void staged_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt is six bits");
@@ -400,6 +408,150 @@ __global__ __launch_bounds__(kThreads) void gemv_resident_kernel(GemvArgs a) {
     }
 }
 
+// ---------------------------------------------------- resident kernel, LDS ring
+
+// The same walk as gemv_resident_kernel, with the weight windows staged through
+// a per-wave LDS ring instead of registers.  One item row (64 blocks, 2176
+// contiguous bytes) arrives by three direct-to-LDS copies marked non-temporal:
+// two of 1 KB (16 bytes per lane) and one of 256 bytes (4 bytes per lane, the
+// first 128 the item's tail).  Contiguous, whole-line copies let the stream use
+// the non-temporal policy that the 36-byte per-lane windows cannot.  Each lane
+// then reads its block's 36-byte window from the slot.  The copies are inline
+// assembly (the compiler would otherwise wait for all of them before every LDS
+// read); their waits are explicit.  Needs 16-byte aligned rows (k a multiple
+// of 256) and a 16-byte aligned matrix.
+constexpr int kItemBytes = 64 * kBlockBytes;  // 2176
+constexpr int kSlotBytes = 2304;              // 2048 + the 256-byte copy
+constexpr int kCopiesPerItemRow = 3;
+
+__device__ __forceinline__ void copy_nt16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t off) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(off), "s"(r), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void copy_nt4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t off) {
+    asm volatile("buffer_load_dword %0, %1, 0 offen nt lds" ::"v"(off), "s"(r), "{m0}"(lds) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds_reads() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Copy item rows [item_base + m * row_bytes, + item_len) into the slot at LDS
+// address `slot`.  item_base is kOob for a dead refill: every copy then reads
+// zeros (bit 31 stays set).
+template <int MR>
+__device__ __forceinline__ void copy_item(const WeightStream &ws, uint32_t item_base, uint32_t item_len, int lane,
+                                          uint32_t slot) {
+    const uint32_t o0 = 16 * lane, o1 = 1024 + 16 * lane, o2 = 2048 + 4 * lane;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        const uint32_t row = item_base + m * ws.row_bytes;
+        copy_nt16(ws.rsrc, slot + m * kSlotBytes, (row + o0) | oob_bit(o0 < item_len));
+        copy_nt16(ws.rsrc, slot + m * kSlotBytes + 1024, (row + o1) | oob_bit(o1 < item_len));
+        copy_nt4(ws.rsrc, slot + m * kSlotBytes + 2048, (row + o2) | oob_bit(o2 < item_len));
+    }
+}
+
+template <int MR>
+__device__ __forceinline__ void read_item(const uint8_t *slot, uint32_t lane_part, Window (&win)[MR]) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(slot + m * kSlotBytes + lane_part);
+#pragma unroll
+        for (int i = 0; i < 9; ++i) win[m].d[i] = p[i];
+    }
+}
+
+__host__ __device__ inline size_t ring_lds_offset(int rows, int words, int kt) {
+    return ((stack_bytes(rows, words, kt) + 15) & ~size_t(15)) + static_cast<size_t>(kWaves) * kOutPerWave * 8;
+}
+
+template <int R, int WORDS, int MR, int P>
+__global__ __launch_bounds__(kThreads) void gemv_ring_kernel(GemvArgs a) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+    const int G = gw < a.num_groups ? static_cast<int>((a.num_groups - gw + stride - 1) / stride) : 0;
+    const int ub = a.ub;
+    const int T = G * ub;
+    const size_t totals_at = (stack_bytes(R, WORDS, a.kt) + 15) & ~size_t(15);
+    double *totals = reinterpret_cast<double *>(lds + totals_at) + wave * kOutPerWave;
+    uint8_t *ring = lds + ring_lds_offset(R, WORDS, a.kt) + wave * (P * MR * kSlotBytes);
+    const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((uintptr_t)(lptr_t)ring));
+
+    WeightStream ws;
+    ws.row_bytes = static_cast<uint32_t>(a.nb) * kBlockBytes;
+    ws.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.w), 0,
+                                                static_cast<int>(static_cast<uint32_t>(a.n) * ws.row_bytes),
+                                                kBufferDword3);
+    ws.lane_part = static_cast<uint32_t>(lane * kBlockBytes) & ~3u;
+    const uint32_t group_bytes = ws.row_bytes * MR;
+    const uint32_t grid_group_bytes = static_cast<uint32_t>(stride) * group_bytes;
+    const uint32_t first_group_bytes = static_cast<uint32_t>(gw) * group_bytes;
+    auto item_base = [&](const Cursor &c) -> uint32_t {
+        return c.gi < G ? first_group_bytes + c.gi * grid_group_bytes + c.u * kItemBytes : kOob;
+    };
+    auto item_len = [&](const Cursor &c) -> uint32_t {
+        return static_cast<uint32_t>(min(64, a.nb - c.u * 64)) * kBlockBytes;
+    };
+
+    // Prologue: stage the stack, put the first P items in flight, barrier once
+    // the stack has landed.
+    stage_tile<R, WORDS>(a, lds, 0, wave, lane);
+    Cursor ahead{0, 0};
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        copy_item<MR>(ws, item_base(ahead), item_len(ahead), lane, ring_lds + p * MR * kSlotBytes);
+        ahead.next(ub);
+    }
+    staged_barrier<P * MR * kCopiesPerItemRow>();
+
+    double acc[MR][R];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[m][r] = 0.0;
+
+    Cursor cur{0, 0};
+    for (int t0 = 0; t0 < T; t0 += P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            wait_vm<(P - 1) * MR * kCopiesPerItemRow>();  // this item's copies have landed
+            Window win[MR];
+            read_item<MR>(ring + p * MR * kSlotBytes, ws.lane_part, win);
+            const Item it{gw + static_cast<int64_t>(cur.gi) * stride, 0, cur.u};
+            compute_item<R, WORDS, MR>(a, lds, it, lane, win, acc);
+            wait_lds_reads();  // the slot is read before it is refilled
+            copy_item<MR>(ws, item_base(ahead), item_len(ahead), lane, ring_lds + p * MR * kSlotBytes);
+            ahead.next(ub);
+            if (cur.gi < G && cur.u == ub - 1) {
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const double tot = wave_sum(acc[m][r]);
+                        acc[m][r] = 0.0;
+                        if (lane == 0) totals[(cur.gi * MR + m) * R + r] = tot;
+                    }
+            }
+            cur.next(ub);
+        }
+    }
+    wait_vm<0>();  // the dead refills read nothing but still write the ring
+    const double post = WORDS == 2 ? 1.0 / 128.0 : 1.0;
+    wave_lds_sync();  // lane 0 parked the totals the whole wave reads now
+    for (int i = lane; i < G * MR * R; i += 64) {
+        const int gi = i / (MR * R), m = (i / R) % MR, r = i % R;
+        const int64_t row = (gw + static_cast<int64_t>(gi) * stride) * MR + m;
+        if (row < a.n) write_output(a, r, row, totals[i] * post);
+    }
+}
+
 // --------------------------------------------------------------- tiled kernel
 
 // The stack is staged one column tile at a time; each wave owns one row group and
@@ -486,7 +638,12 @@ hipError_t run(GemvArgs a, hipStream_t stream) {
         waves = std::max<int64_t>(waves, min_waves);
         const int64_t grid = (waves + kWaves - 1) / kWaves;
         const size_t lds = ((stack + 15) & ~size_t(15)) + static_cast<size_t>(kWaves) * kOutPerWave * 8;
-        gemv_resident_kernel<R, WORDS, MR, P><<<dim3(static_cast<unsigned>(grid)), kThreads, lds, stream>>>(a);
+        const size_t ring_lds = ring_lds_offset(R, WORDS, a.kt) + static_cast<size_t>(kWaves) * P * MR * kSlotBytes;
+        const bool aligned = (row_bytes % 16) == 0 && (reinterpret_cast<uintptr_t>(a.w) & 15) == 0;
+        if (aligned && ring_lds * 2 <= static_cast<size_t>(dev.lds_per_block))
+            gemv_ring_kernel<R, WORDS, MR, P><<<dim3(static_cast<unsigned>(grid)), kThreads, ring_lds, stream>>>(a);
+        else
+            gemv_resident_kernel<R, WORDS, MR, P><<<dim3(static_cast<unsigned>(grid)), kThreads, lds, stream>>>(a);
     } else {
         const int64_t grid = (a.num_groups + kWaves - 1) / kWaves;
         gemv_tiled_kernel<R, WORDS, MR><<<dim3(static_cast<unsigned>(grid)), kThreads, stack, stream>>>(a);

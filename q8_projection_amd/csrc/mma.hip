@@ -11,10 +11,10 @@
 // the activation words and the activation block scales into one slot of an LDS
 // ring.  The copies are direct-to-LDS buffer loads: each instruction moves
 // 1 KB, every lane 16 contiguous bytes, so HBM sees whole contiguous runs and
-// no VGPR holds staged data.  The four waves of the workgroup issue the copies
-// together and split the chunk's blocks for the math; one barrier per chunk
-// hands a ring slot from the copies to the MFMAs, and the copies run
-// kDepth - 1 chunks ahead.
+// no VGPR holds staged data.  The W waves of the workgroup issue the copies
+// together (each lane's offsets are computed once; a chunk adds a constant) and
+// split the chunk's blocks for the math; one barrier per chunk hands a ring
+// slot from the copies to the MFMAs, and the copies run kDepth - 1 chunks ahead.
 //
 // Math.  v_mfma_i32_16x16x32_i8 takes one block per instruction: operand A is
 // 16 activation columns, operand B 16 weight rows, both 32 int8 along K, and the
@@ -24,8 +24,8 @@
 // a tile are the hi and lo words of 8 activation rows, ordered so that each lane
 // receives both words of two rows: T = 128 S_hi + S_lo is formed exactly in
 // int32.  Every block term (d * s) * T is accumulated in f64; at the end the
-// four waves' partials are added in a fixed order and each output is rounded
-// once to f32.
+// waves' partials are added pairwise in a fixed tree order and each output is
+// rounded once to f32.
 //
 // The copies are issued with inline assembly on purpose: the compiler cannot
 // tell ring slots apart and would otherwise wait for every outstanding copy
@@ -41,12 +41,11 @@ namespace {
 
 #pragma clang fp contract(off)
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr int kChunkBlocks = 8;                            // blocks per chunk
 constexpr int kRowChunk = kChunkBlocks * kBlockBytes;      // 272 bytes of one weight row
 constexpr int kRowGranules = kRowChunk / 16;               // 17
 constexpr int kActChunk = kChunkBlocks * kBlock;           // 256 activation bytes per row and word
+constexpr int kTileBytes = 16 * kActChunk;                 // one 16-column activation tile
 constexpr int kCopyBytes = 1024;                           // one copy instruction: 64 lanes x 16 B
 constexpr int kRingBudget = 144 * 1024;
 constexpr int kMaxDepth = 12;
@@ -57,25 +56,34 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t *lds_ptr_t;
 
 // Sizes of one ring slot and of the ring, per instantiation.
-//   RT: 16-row weight tiles per workgroup; AT: 16-column activation tiles.
-template <int RT, int AT, int WORDS>
+//   RT: 16-row weight tiles per workgroup; TT: 16-column activation tiles;
+//   GA x GB waves: wave w takes activation tiles of group w % GA and blocks of
+//   group w / GA of every chunk.
+template <int RT, int TT, int WORDS, int GA, int GB>
 struct Layout {
+    static constexpr int W = GA * GB;                          // waves per workgroup
+    static constexpr int kAT = TT / GA;                        // activation tiles per wave
     static constexpr int kRows = RT * 16;                      // weight rows a workgroup may own
-    static constexpr int kActRows = AT * 16 / WORDS;           // activation rows the tiles hold
+    static constexpr int kActRows = TT * 16 / WORDS;           // activation rows the tiles hold
     static constexpr int kWCopies = (kRows * kRowGranules + 63) / 64;
-    static constexpr int kACopies = AT * 4;                    // 16 columns x 256 B per tile
+    static constexpr int kACopies = TT * 4;                    // 16 columns x 256 B per tile
     static constexpr int kSCopies = (kActRows * 2 + 63) / 64;  // 8 f32 scales (2 granules) per row
     static constexpr int kCopies = kWCopies + kACopies + kSCopies;
-    static constexpr int kPerWave = (kCopies + kWaves - 1) / kWaves;
-    static constexpr int kSlotBytes = kPerWave * kWaves * kCopyBytes;  // tail copies are dummies
+    static constexpr int kPerWave = (kCopies + W - 1) / W;     // copies past kCopies are dummies
+    static constexpr int kSlotBytes = kCopies * kCopyBytes;
     static constexpr int kAOff = kWCopies * kCopyBytes;
     static constexpr int kSOff = kAOff + kACopies * kCopyBytes;
-    static constexpr int kDepth = std::min(kMaxDepth, kRingBudget / kSlotBytes);
+    static constexpr int kDepth = std::min(kMaxDepth, (kRingBudget - kCopyBytes) / kSlotBytes);
+    static constexpr int kDummy = kDepth * kSlotBytes;         // 1 KB the dummy copies write
+    static constexpr int kBlocksPerWave = kChunkBlocks / GB;
     static constexpr int kVals = WORDS == 2 ? 2 : 4;           // f64 accumulators per lane and tile pair
-    static constexpr int kRedBytes = kWaves * RT * AT * kVals * 64 * 8;
-    static constexpr int kLdsBytes = std::max(kDepth * kSlotBytes, kRedBytes);
+    static constexpr int kAccBytes = RT * kAT * kVals * 64 * 8; // one wave's accumulators
+    static constexpr int kLdsBytes = std::max(kDummy + kCopyBytes, (W / 2) * kAccBytes);
+    static_assert(TT % GA == 0 && kChunkBlocks % GB == 0 && (GB & (GB - 1)) == 0, "wave split");
+    static_assert(W <= 16, "at most 1024 threads");
     static_assert(kDepth >= 3, "the ring needs at least three slots");
     static_assert(kPerWave * (kDepth - 2) <= 63, "outstanding copies exceed the vmcnt range");
+    static_assert(RT * TT * kVals * 64 * 8 <= kLdsBytes, "room for the totals");
 };
 
 struct MmaArgs {
@@ -111,8 +119,9 @@ __device__ __forceinline__ void wait_copies() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Hand a ring slot over: this wave's LDS reads are complete (release) and the
-// other waves' copies, already waited for with vmcnt, are visible (acquire).
+// Hand LDS over between waves: this wave's LDS accesses are complete (release)
+// and the other waves' (including copies already waited for with vmcnt) are
+// visible (acquire).
 __device__ __forceinline__ void ring_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
@@ -131,115 +140,138 @@ __device__ __forceinline__ int act_slot(int m) {
         return m;
 }
 
+// What copy i of a chunk reads.  Layout of a slot:
+//   [0, kAOff)      weight rows, row-major, 272 bytes each (17 granules)
+//   [kAOff, kSOff)  activation tiles: 16 column slots x 256 bytes, the 16-byte
+//                   granules of slot s XOR-permuted by s
+//   [kSOff, ...)    activation scales, [row][8] f32
+// The result is this lane's offset for chunk 0 (bit 31 set where the lane reads
+// nothing); chunk c adds c * 272, c * 256 or c * 32 to it.
+template <int RT, int TT, int WORDS, int GA, int GB>
+__device__ __forceinline__ uint32_t plan_copy(const MmaArgs &a, int i, int lane, uint32_t r0, int rcount) {
+    using L = Layout<RT, TT, WORDS, GA, GB>;
+    if (i < L::kWCopies) {
+        const int g = i * 64 + lane;
+        const int row = g / kRowGranules;
+        const int part = g - row * kRowGranules;
+        return ((r0 + row) * a.row_bytes + 16 * part) | oob_bit(row < rcount);
+    }
+    if (i < L::kWCopies + L::kACopies) {
+        const int ia = i - L::kWCopies;
+        const int t = ia >> 2;
+        const int s = ((ia & 3) << 2) + (lane >> 4);  // column slot
+        const int g = (lane & 15) ^ s;                // granule of the row's 256 chunk bytes
+        const int row = WORDS == 2 ? t * 8 + (s & 7) : t * 16 + s;
+        return (static_cast<uint32_t>(row) * a.k + 16 * g) | oob_bit(row < a.rows);
+    }
+    if (i < L::kCopies) {
+        const int g = (i - L::kWCopies - L::kACopies) * 64 + lane;
+        const int row = g >> 1;
+        return (static_cast<uint32_t>(row) * a.nb * 4 + 16 * (g & 1)) | oob_bit(row < a.rows);
+    }
+    return kOob;
+}
+
 // Copies of chunk c into the slot at LDS address `slot`.  Every wave issues
-// exactly kPerWave copies (tail copies read nothing), so the vmcnt waits are
-// exact.  Layout of a slot:
-//   [0, kAOff)           weight rows, row-major, 272 bytes each (17 granules)
-//   [kAOff, kSOff)       activation tiles: 16 column slots x 256 bytes, the
-//                        16-byte granules of slot s XOR-permuted by s
-//   [kSOff, ...)         activation scales, [row][8] f32
-template <int RT, int AT, int WORDS>
-__device__ __forceinline__ void issue_chunk(const MmaArgs &a, const Rsrcs &rs, uint32_t slot, int c, int wave,
-                                            int lane, uint32_t r0, int rcount) {
-    using L = Layout<RT, AT, WORDS>;
-    const bool chunk_ok = c < a.nchunks;
+// exactly kPerWave copies, so the vmcnt waits are exact.
+template <int RT, int TT, int WORDS, int GA, int GB>
+__device__ __forceinline__ void issue_chunk(const Rsrcs &rs,
+                                            const uint32_t (&base)[Layout<RT, TT, WORDS, GA, GB>::kPerWave],
+                                            uint32_t slot, uint32_t dummy, int c, int nchunks, int wave) {
+    using L = Layout<RT, TT, WORDS, GA, GB>;
+    constexpr int W = L::W;
+    const uint32_t chunk_oob = c < nchunks ? 0u : kOob;
 #pragma unroll
     for (int u = 0; u < L::kPerWave; ++u) {
-        const int i = wave + kWaves * u;  // wave-uniform copy index
-        __amdgpu_buffer_rsrc_t r = rs.w;
-        uint32_t off = kOob;
-        if (i < L::kWCopies) {
-            const int g = i * 64 + lane;
-            const int row = g / kRowGranules;
-            const int part = g - row * kRowGranules;
-            const bool ok = chunk_ok && row < rcount;
-            off = ((r0 + row) * a.row_bytes + c * kRowChunk + 16 * part) | oob_bit(ok);
+        const int i = wave + W * u;  // wave-uniform copy index
+        if (i >= L::kCopies) {
+            copy16(rs.w, dummy, kOob);
+        } else if (i < L::kWCopies) {
+            copy16(rs.w, slot + i * kCopyBytes, (base[u] + c * kRowChunk) | chunk_oob);
         } else if (i < L::kWCopies + L::kACopies) {
-            const int ia = i - L::kWCopies;
-            const int t = ia >> 2;
-            const int s = ((ia & 3) << 2) + (lane >> 4);  // column slot
-            const int g = (lane & 15) ^ s;                // granule of the row's 256 chunk bytes
-            int row;
-            if constexpr (WORDS == 2) {
-                row = t * 8 + (s & 7);
-                r = (ia & 2) ? rs.lo : rs.hi;
-            } else {
-                row = t * 16 + s;
-                r = rs.hi;
-            }
-            const bool ok = chunk_ok && row < a.rows;
-            off = (static_cast<uint32_t>(row) * a.k + c * kActChunk + 16 * g) | oob_bit(ok);
-        } else if (i < L::kCopies) {
-            const int g = (i - L::kWCopies - L::kACopies) * 64 + lane;
-            const int row = g >> 1;
-            const bool ok = chunk_ok && row < a.rows;
-            r = rs.s;
-            off = (static_cast<uint32_t>(row) * a.nb * 4 + c * (kChunkBlocks * 4) + 16 * (g & 1)) | oob_bit(ok);
+            const bool lo = WORDS == 2 && ((i - L::kWCopies) & 2);
+            copy16(lo ? rs.lo : rs.hi, slot + i * kCopyBytes, (base[u] + c * kActChunk) | chunk_oob);
+        } else {
+            copy16(rs.s, slot + i * kCopyBytes, (base[u] + c * (kChunkBlocks * 4)) | chunk_oob);
         }
-        copy16(r, slot + i * kCopyBytes, off);
     }
 }
 
-// The math of one chunk for this wave: blocks wave and wave + 4 of the slot.
-template <int RT, int AT, int WORDS>
-__device__ __forceinline__ void compute_chunk(const uint8_t *slot, int wave, int lane,
-                                              double (&acc)[RT][AT][Layout<RT, AT, WORDS>::kVals]) {
-    using L = Layout<RT, AT, WORDS>;
-    const int q = lane >> 4;   // operand k-quarter; result column group
-    const int c16 = lane & 15; // operand column (A) / weight row (B and result)
+// Lane-constant LDS offsets (relative to a slot) of one block's operands.
+struct BlockOffsets {
+    uint32_t a;    // activation operand of the wave's first tile (its tile t: + t * kTileBytes)
+    uint32_t b;    // dword-aligned start of the weight operand of row tile 0 (+ rt * 16 * 272)
+    uint32_t d;    // the weight row's block scale (+ rt * 16 * 272)
+    uint32_t s;    // activation scale of the lane's first result column, the wave's first tile
+    uint32_t sel;  // v_perm selector realigning the weight operand (uniform)
+};
+
+template <int RT, int TT, int WORDS, int GA, int GB>
+__device__ __forceinline__ BlockOffsets block_offsets(int j, int t0, int lane) {
+    using L = Layout<RT, TT, WORDS, GA, GB>;
+    const int q = lane >> 4, c16 = lane & 15;
     const int as = act_slot<WORDS>(c16);
+    const int boff = j * kBlockBytes + 2 + 8 * q;  // first quant byte of the lane's weight operand
+    BlockOffsets o;
+    o.a = L::kAOff + t0 * kTileBytes + as * kActChunk + ((((j << 1) + (q >> 1)) ^ as) << 4) + ((q & 1) << 3);
+    o.b = c16 * kRowChunk + (boff & ~3);
+    o.d = c16 * kRowChunk + j * kBlockBytes;
+    o.s = L::kSOff + (t0 * (16 / WORDS) + (WORDS == 2 ? 2 * q : 4 * q)) * (kChunkBlocks * 4) + 4 * j;
+    o.sel = (boff & 2) ? 0x05040302u : 0x03020100u;
+    return o;
+}
+
+// The math of one block of the slot for this wave.
+template <int RT, int TT, int WORDS, int GA, int GB>
+__device__ __forceinline__ void compute_block(const uint8_t *slot, const BlockOffsets &o,
+                                              double (&acc)[RT][Layout<RT, TT, WORDS, GA, GB>::kAT][Layout<RT, TT, WORDS, GA, GB>::kVals]) {
+    using L = Layout<RT, TT, WORDS, GA, GB>;
+    constexpr int AT = L::kAT;
+    long aop[AT];
+    double s[AT][L::kVals];
 #pragma unroll
-    for (int jj = 0; jj < kChunkBlocks / kWaves; ++jj) {
-        const int j = wave + kWaves * jj;  // wave-uniform block of the chunk
-        long aop[AT];
-        double s[AT][L::kVals];
+    for (int t = 0; t < AT; ++t) {
+        aop[t] = *reinterpret_cast<const long *>(slot + o.a + t * kTileBytes);
+#pragma unroll
+        for (int v = 0; v < L::kVals; ++v)
+            s[t][v] = static_cast<double>(*reinterpret_cast<const float *>(
+                slot + o.s + (t * (16 / WORDS) + v) * (kChunkBlocks * 4)));
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const uint32_t *pw = reinterpret_cast<const uint32_t *>(slot + o.b + rt * 16 * kRowChunk);
+        const uint32_t w0 = pw[0], w1 = pw[1], w2 = pw[2];
+        const uint32_t lo32 = __builtin_amdgcn_perm(w1, w0, o.sel);
+        const uint32_t hi32 = __builtin_amdgcn_perm(w2, w1, o.sel);
+        const long bop = static_cast<long>((static_cast<uint64_t>(hi32) << 32) | lo32);
+        const uint16_t dbits = *reinterpret_cast<const uint16_t *>(slot + o.d + rt * 16 * kRowChunk);
+        const double d = static_cast<double>(f16_bits_to_float(dbits));
 #pragma unroll
         for (int t = 0; t < AT; ++t) {
-            const uint8_t *pa = slot + L::kAOff + t * 4096 + as * 256 + ((((j << 1) + (q >> 1)) ^ as) << 4) + ((q & 1) << 3);
-            aop[t] = *reinterpret_cast<const long *>(pa);
-            const float *ps = reinterpret_cast<const float *>(slot + L::kSOff);
+            const v4i sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[t], bop, v4i{0, 0, 0, 0}, 0, 0, 0);
+            if constexpr (WORDS == 2) {
+                const int t0 = sum[0] * 128 + sum[1];
+                const int t1 = sum[2] * 128 + sum[3];
+                acc[rt][t][0] = __builtin_fma(d * s[t][0], static_cast<double>(t0), acc[rt][t][0]);
+                acc[rt][t][1] = __builtin_fma(d * s[t][1], static_cast<double>(t1), acc[rt][t][1]);
+            } else {
 #pragma unroll
-            for (int v = 0; v < L::kVals; ++v) {
-                const int row = WORDS == 2 ? t * 8 + 2 * q + v : t * 16 + 4 * q + v;
-                s[t][v] = static_cast<double>(ps[row * kChunkBlocks + j]);
-            }
-        }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const uint8_t *prow = slot + (rt * 16 + c16) * kRowChunk;
-            const int boff = j * kBlockBytes + 2 + 8 * q;  // first quant byte of this lane's operand
-            const uint32_t *pw = reinterpret_cast<const uint32_t *>(prow + (boff & ~3));
-            const uint32_t w0 = pw[0], w1 = pw[1], w2 = pw[2];
-            const uint32_t sel = (boff & 2) ? 0x05040302u : 0x03020100u;
-            const uint32_t lo32 = __builtin_amdgcn_perm(w1, w0, sel);
-            const uint32_t hi32 = __builtin_amdgcn_perm(w2, w1, sel);
-            const long bop = static_cast<long>((static_cast<uint64_t>(hi32) << 32) | lo32);
-            const uint16_t dbits = *reinterpret_cast<const uint16_t *>(prow + j * kBlockBytes);
-            const double d = static_cast<double>(f16_bits_to_float(dbits));
-#pragma unroll
-            for (int t = 0; t < AT; ++t) {
-                const v4i dsum = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[t], bop, v4i{0, 0, 0, 0}, 0, 0, 0);
-                if constexpr (WORDS == 2) {
-                    const int t0 = dsum[0] * 128 + dsum[1];
-                    const int t1 = dsum[2] * 128 + dsum[3];
-                    acc[rt][t][0] = __builtin_fma(d * s[t][0], static_cast<double>(t0), acc[rt][t][0]);
-                    acc[rt][t][1] = __builtin_fma(d * s[t][1], static_cast<double>(t1), acc[rt][t][1]);
-                } else {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        acc[rt][t][v] = __builtin_fma(d * s[t][v], static_cast<double>(dsum[v]), acc[rt][t][v]);
-                }
+                for (int v = 0; v < 4; ++v)
+                    acc[rt][t][v] = __builtin_fma(d * s[t][v], static_cast<double>(sum[v]), acc[rt][t][v]);
             }
         }
     }
 }
 
-template <int RT, int AT, int WORDS>
-__global__ __launch_bounds__(kThreads, 1) void mma_kernel(MmaArgs a) {
-    using L = Layout<RT, AT, WORDS>;
+template <int RT, int TT, int WORDS, int GA, int GB>
+__global__ __launch_bounds__(64 * GA * GB, 1) void mma_kernel(MmaArgs a) {
+    using L = Layout<RT, TT, WORDS, GA, GB>;
+    constexpr int W = L::W;
+    constexpr int AT = L::kAT;
     extern __shared__ __align__(16) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ga = wave % GA, gb = wave / GA;
     const uint32_t r0 = blockIdx.x * static_cast<uint32_t>(a.rows_per_wg);
     const int rcount = static_cast<int>(min(static_cast<uint32_t>(a.rows_per_wg), a.n - r0));
 
@@ -251,8 +283,16 @@ __global__ __launch_bounds__(kThreads, 1) void mma_kernel(MmaArgs a) {
                        : rs.hi;
     rs.s = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.scale), 0,
                                              static_cast<uint32_t>(a.rows) * a.nb * 4, kBufferDword3);
-
     const uint32_t base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((uintptr_t)(lds_ptr_t)smem));
+
+    uint32_t plan[L::kPerWave];
+#pragma unroll
+    for (int u = 0; u < L::kPerWave; ++u)
+        plan[u] = plan_copy<RT, TT, WORDS, GA, GB>(a, wave + W * u, lane, r0, rcount);
+    BlockOffsets offs[L::kBlocksPerWave];
+#pragma unroll
+    for (int jj = 0; jj < L::kBlocksPerWave; ++jj)
+        offs[jj] = block_offsets<RT, TT, WORDS, GA, GB>(gb + GB * jj, ga * AT, lane);
 
     double acc[RT][AT][L::kVals];
 #pragma unroll
@@ -265,37 +305,70 @@ __global__ __launch_bounds__(kThreads, 1) void mma_kernel(MmaArgs a) {
     // Prologue: chunks 0 .. kDepth-2 in flight.
 #pragma unroll
     for (int c = 0; c < L::kDepth - 1; ++c)
-        issue_chunk<RT, AT, WORDS>(a, rs, base + c * L::kSlotBytes, c, wave, lane, r0, rcount);
+        issue_chunk<RT, TT, WORDS, GA, GB>(rs, plan, base + c * L::kSlotBytes, base + L::kDummy, c, a.nchunks, wave);
 
     int cur = 0;                 // slot of chunk c
     int nxt = L::kDepth - 1;     // slot of chunk c + kDepth - 1
     for (int c = 0; c < a.nchunks; ++c) {
         wait_copies<L::kPerWave * (L::kDepth - 2)>();  // this wave's copies of chunk c have landed
         ring_barrier();                                // everyone's have; slot nxt is free
-        issue_chunk<RT, AT, WORDS>(a, rs, base + nxt * L::kSlotBytes, c + L::kDepth - 1, wave, lane, r0, rcount);
-        compute_chunk<RT, AT, WORDS>(smem + cur * L::kSlotBytes, wave, lane, acc);
+        issue_chunk<RT, TT, WORDS, GA, GB>(rs, plan, base + nxt * L::kSlotBytes, base + L::kDummy,
+                                           c + L::kDepth - 1, a.nchunks, wave);
+        const uint8_t *slot = smem + cur * L::kSlotBytes;
+#pragma unroll
+        for (int jj = 0; jj < L::kBlocksPerWave; ++jj) compute_block<RT, TT, WORDS, GA, GB>(slot, offs[jj], acc);
         cur = cur + 1 == L::kDepth ? 0 : cur + 1;
         nxt = nxt + 1 == L::kDepth ? 0 : nxt + 1;
     }
     wait_copies<0>();  // the trailing copies read nothing but still write the ring
     ring_barrier();
 
-    // Partials of the four waves, summed in a fixed order.
+    // Pairwise tree over the block groups of each activation group: at each
+    // level the upper half parks its accumulators in LDS and the lower half
+    // adds them (fixed order).
     double *red = reinterpret_cast<double *>(smem);
+    constexpr int kAccVals = RT * AT * L::kVals;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int half = GB / 2; half >= 1; half >>= 1) {
+        if (gb >= half && gb < 2 * half) {
+            double *dst = red + (ga + GA * (gb - half)) * kAccVals * 64;
 #pragma unroll
-        for (int t = 0; t < AT; ++t)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int v = 0; v < L::kVals; ++v)
-                red[(((wave * RT + rt) * AT + t) * L::kVals + v) * 64 + lane] = acc[rt][t][v];
+                for (int t = 0; t < AT; ++t)
+#pragma unroll
+                    for (int v = 0; v < L::kVals; ++v) dst[((rt * AT + t) * L::kVals + v) * 64 + lane] = acc[rt][t][v];
+        }
+        ring_barrier();
+        if (gb < half) {
+            const double *src = red + (ga + GA * gb) * kAccVals * 64;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int t = 0; t < AT; ++t)
+#pragma unroll
+                    for (int v = 0; v < L::kVals; ++v) acc[rt][t][v] += src[((rt * AT + t) * L::kVals + v) * 64 + lane];
+        }
+        ring_barrier();
+    }
+    // The waves of block group 0 hold the totals of their tiles; park them as
+    // [rt][tile][v][lane] and let every wave write a share of the outputs.
+    if (gb == 0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int t = 0; t < AT; ++t)
+#pragma unroll
+                for (int v = 0; v < L::kVals; ++v)
+                    red[((rt * TT + ga * AT + t) * L::kVals + v) * 64 + lane] = acc[rt][t][v];
+    }
     ring_barrier();
 
     const double post = WORDS == 2 ? 1.0 / 128.0 : 1.0;
     const int q = lane >> 4;
     const int c16 = lane & 15;
-    for (int p = wave; p < RT * AT; p += kWaves) {
-        const int rt = p / AT, t = p - (p / AT) * AT;
+    for (int p = wave; p < RT * TT; p += W) {
+        const int rt = p / TT, t = p - (p / TT) * TT;
         const int row = rt * 16 + c16;
         if (row >= rcount) continue;
         const uint32_t n = r0 + row;
@@ -303,9 +376,7 @@ __global__ __launch_bounds__(kThreads, 1) void mma_kernel(MmaArgs a) {
         for (int v = 0; v < L::kVals; ++v) {
             const int ar = WORDS == 2 ? t * 8 + 2 * q + v : t * 16 + 4 * q + v;
             if (ar >= a.rows) continue;
-            double tot = red[(((0 * RT + rt) * AT + t) * L::kVals + v) * 64 + lane];
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w) tot += red[(((w * RT + rt) * AT + t) * L::kVals + v) * 64 + lane];
+            const double tot = red[(p * L::kVals + v) * 64 + lane];
             const int64_t o = static_cast<int64_t>(ar) * a.ldy + n;
             const double res = a.residual ? static_cast<double>(a.residual[o]) : 0.0;
             a.y[o] = static_cast<float>(tot * post + res);
@@ -313,20 +384,25 @@ __global__ __launch_bounds__(kThreads, 1) void mma_kernel(MmaArgs a) {
     }
 }
 
-template <int RT, int AT, int WORDS>
+template <int RT, int TT, int WORDS, int GA, int GB>
 hipError_t run(const MmaArgs &a, hipStream_t stream) {
-    using L = Layout<RT, AT, WORDS>;
+    using L = Layout<RT, TT, WORDS, GA, GB>;
     if (L::kLdsBytes > device_info().lds_per_block) return hipErrorInvalidConfiguration;
     const uint32_t grid = (a.n + a.rows_per_wg - 1) / a.rows_per_wg;
-    hipLaunchKernelGGL((mma_kernel<RT, AT, WORDS>), dim3(grid), dim3(kThreads), L::kLdsBytes, stream, a);
+    hipLaunchKernelGGL((mma_kernel<RT, TT, WORDS, GA, GB>), dim3(grid), dim3(64 * L::W), L::kLdsBytes, stream, a);
     return hipGetLastError();
 }
 
-template <int WORDS, int AT>
+// Wave split per activation-tile count: one tile, eight block groups; two
+// tiles, one per wave, four block groups; four or eight tiles, four activation
+// groups by four block groups (sixteen waves).
+template <int WORDS, int TT>
 hipError_t by_rt(int rt, const MmaArgs &a, hipStream_t s) {
-    if (rt == 1) return run<1, AT, WORDS>(a, s);
-    if (rt == 2) return run<2, AT, WORDS>(a, s);
-    if constexpr (AT * WORDS <= 4) return run<4, AT, WORDS>(a, s);
+    constexpr int GA = TT == 1 ? 1 : TT == 2 ? 2 : 4;
+    constexpr int GB = TT == 1 ? 8 : 4;
+    if (rt == 1) return run<1, TT, WORDS, GA, GB>(a, s);
+    if (rt == 2) return run<2, TT, WORDS, GA, GB>(a, s);
+    if constexpr (TT * WORDS <= 4) return run<4, TT, WORDS, GA, GB>(a, s);
     return hipErrorInvalidValue;
 }
 
