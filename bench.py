@@ -57,18 +57,21 @@ def kernel_hash(sources) -> str:
 
 
 def stored_traffic(call_name: str):
-    """HBM bytes per launch of a call from its committed counter summary
-    (profiles/<call>_*counters.txt), or None if there is none or it was taken on
-    kernel sources other than the current ones."""
+    """HBM bytes per launch of a call from its committed counter summary (the
+    profiles/*counters.txt whose `call` field names it), or None if there is none
+    or it was taken on kernel sources other than the current ones."""
     try:
-        names = [f for f in os.listdir(PROFILES) if f.startswith(call_name + "_") and f.endswith("counters.txt")]
-        for fname in names:
+        for fname in sorted(os.listdir(PROFILES)):
+            if not fname.endswith("counters.txt"):
+                continue
             fields = {}
             with open(os.path.join(PROFILES, fname)) as f:
                 for line in f:
                     if "=" in line and not line.lstrip().startswith("#"):
                         k, v = line.split("=", 1)
                         fields[k.strip()] = v.strip()
+            if fields.get("call") != call_name:
+                continue
             sources = fields.get("kernel_sources", "").split()
             if sources and fields.get("kernel_sources_sha256_16") == kernel_hash(sources):
                 return float(fields["hbm_bytes_per_launch"])
@@ -286,7 +289,8 @@ def main(argv=None):
                                  "project_us": round(tp * 1e6, 3), "quantize_us": round(tq * 1e6, 3),
                                  "GBps": round(p.call.weight_bytes / tp / 1e9, 1),
                                  "pct_hbm_peak": round(p.call.weight_bytes / tp / 1e9 / HBM_PEAK_GBPS * 100, 1),
-                                 "rows_GFLOPs": round(p.call.flops / tp / 1e9, 1)}
+                                 "rows_GFLOPs": round(p.call.flops / tp / 1e9, 1),
+                                 "hbm_bytes_counted": stored_traffic(p.call.name)}
     by_rows = {}
     for name, d in per_call.items():
         key = str(d["rows"])

@@ -23,9 +23,10 @@ def test_counter_summary_is_keyed_on_its_sources(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     h = bench.kernel_hash(["k.hip"])
     (tmp_path / "demo_counters.txt").write_text(
-        f"# comment = ignored\nkernel_sources = k.hip\nkernel_sources_sha256_16 = {h}\nhbm_bytes_per_launch = 1234\n")
+        f"# comment = ignored\ncall = demo\nkernel_sources = k.hip\nkernel_sources_sha256_16 = {h}\nhbm_bytes_per_launch = 1234\n")
     assert bench.stored_traffic("demo") == 1234.0
     assert bench.stored_traffic("other") is None
+    assert bench.stored_traffic("dem") is None
     src.write_text("kernel v2")
     assert bench.stored_traffic("demo") is None
     assert os.path.exists(tmp_path / "demo_counters.txt")
