@@ -69,16 +69,16 @@ struct Layout {
     static constexpr int kACopies = TT * 4;                    // 16 columns x 256 B per tile
     static constexpr int kSCopies = (kActRows * 2 + 63) / 64;  // 8 f32 scales (2 granules) per row
     static constexpr int kCopies = kWCopies + kACopies + kSCopies;
-    static constexpr int kPerWave = (kCopies + W - 1) / W;     // copies past kCopies are dummies
+    static constexpr int kPerWave = (kCopies + W - 1) / W;     // copies of the first kCopies % W waves
+    static constexpr int kPerWaveLow = kCopies / W;            // copies of the others
     static constexpr int kSlotBytes = kCopies * kCopyBytes;
     static constexpr int kAOff = kWCopies * kCopyBytes;
     static constexpr int kSOff = kAOff + kACopies * kCopyBytes;
-    static constexpr int kDepth = std::min(kMaxDepth, (kRingBudget - kCopyBytes) / kSlotBytes);
-    static constexpr int kDummy = kDepth * kSlotBytes;         // 1 KB the dummy copies write
+    static constexpr int kDepth = std::min(kMaxDepth, kRingBudget / kSlotBytes);
     static constexpr int kBlocksPerWave = kChunkBlocks / GB;
     static constexpr int kVals = WORDS == 2 ? 2 : 4;           // f64 accumulators per lane and tile pair
     static constexpr int kAccBytes = RT * kAT * kVals * 64 * 8; // one wave's accumulators
-    static constexpr int kLdsBytes = std::max(kDummy + kCopyBytes, (W / 2) * kAccBytes);
+    static constexpr int kLdsBytes = std::max(kDepth * kSlotBytes, (W / 2) * kAccBytes);
     static_assert(TT % GA == 0 && kChunkBlocks % GB == 0 && (GB & (GB - 1)) == 0, "wave split");
     static_assert(W <= 16, "at most 1024 threads");
     static_assert(kDepth >= 3, "the ring needs at least three slots");
@@ -172,12 +172,14 @@ __device__ __forceinline__ uint32_t plan_copy(const MmaArgs &a, int i, int lane,
     return kOob;
 }
 
-// Copies of chunk c into the slot at LDS address `slot`.  Every wave issues
-// exactly kPerWave copies, so the vmcnt waits are exact.
+// Copies of chunk c into the slot at LDS address `slot`: copy i is issued by
+// wave i % W, so a wave issues kPerWave or kPerWaveLow copies per chunk, the
+// same number for every chunk (chunks past the end read nothing), and its
+// vmcnt waits are exact.
 template <int RT, int TT, int WORDS, int GA, int GB>
 __device__ __forceinline__ void issue_chunk(const Rsrcs &rs,
                                             const uint32_t (&base)[Layout<RT, TT, WORDS, GA, GB>::kPerWave],
-                                            uint32_t slot, uint32_t dummy, int c, int nchunks, int wave) {
+                                            uint32_t slot, int c, int nchunks, int wave) {
     using L = Layout<RT, TT, WORDS, GA, GB>;
     constexpr int W = L::W;
     const uint32_t chunk_oob = c < nchunks ? 0u : kOob;
@@ -185,7 +187,7 @@ __device__ __forceinline__ void issue_chunk(const Rsrcs &rs,
     for (int u = 0; u < L::kPerWave; ++u) {
         const int i = wave + W * u;  // wave-uniform copy index
         if (i >= L::kCopies) {
-            copy16(rs.w, dummy, kOob);
+            // not this wave's: the copies are dealt round-robin
         } else if (i < L::kWCopies) {
             copy16(rs.w, slot + i * kCopyBytes, (base[u] + c * kRowChunk) | chunk_oob);
         } else if (i < L::kWCopies + L::kACopies) {
@@ -305,22 +307,27 @@ __global__ __launch_bounds__(64 * GA * GB, 1) void mma_kernel(MmaArgs a) {
     // Prologue: chunks 0 .. kDepth-2 in flight.
 #pragma unroll
     for (int c = 0; c < L::kDepth - 1; ++c)
-        issue_chunk<RT, TT, WORDS, GA, GB>(rs, plan, base + c * L::kSlotBytes, base + L::kDummy, c, a.nchunks, wave);
+        issue_chunk<RT, TT, WORDS, GA, GB>(rs, plan, base + c * L::kSlotBytes, c, a.nchunks, wave);
 
+    const bool more = wave < L::kCopies % W;  // this wave issues kPerWave copies per chunk, else kPerWaveLow
     int cur = 0;                 // slot of chunk c
     int nxt = L::kDepth - 1;     // slot of chunk c + kDepth - 1
     for (int c = 0; c < a.nchunks; ++c) {
-        wait_copies<L::kPerWave * (L::kDepth - 2)>();  // this wave's copies of chunk c have landed
-        ring_barrier();                                // everyone's have; slot nxt is free
-        issue_chunk<RT, TT, WORDS, GA, GB>(rs, plan, base + nxt * L::kSlotBytes, base + L::kDummy,
-                                           c + L::kDepth - 1, a.nchunks, wave);
+        // this wave's copies of chunk c have landed
+        if (more)
+            wait_copies<L::kPerWave * (L::kDepth - 2)>();
+        else
+            wait_copies<L::kPerWaveLow * (L::kDepth - 2)>();
+        ring_barrier();  // everyone's have; slot nxt is free
+        issue_chunk<RT, TT, WORDS, GA, GB>(rs, plan, base + nxt * L::kSlotBytes, c + L::kDepth - 1, a.nchunks,
+                                           wave);
         const uint8_t *slot = smem + cur * L::kSlotBytes;
 #pragma unroll
         for (int jj = 0; jj < L::kBlocksPerWave; ++jj) compute_block<RT, TT, WORDS, GA, GB>(slot, offs[jj], acc);
         cur = cur + 1 == L::kDepth ? 0 : cur + 1;
         nxt = nxt + 1 == L::kDepth ? 0 : nxt + 1;
     }
-    wait_copies<0>();  // the trailing copies read nothing but still write the ring
+    wait_copies<0>();  // the trailing copies read nothing but may still write the ring
     ring_barrier();
 
     // Pairwise tree over the block groups of each activation group: at each
