@@ -49,6 +49,7 @@ constexpr int kTileBytes = 16 * kActChunk;                 // one 16-column acti
 constexpr int kCopyBytes = 1024;                           // one copy instruction: 64 lanes x 16 B
 constexpr int kRingBudget = 144 * 1024;
 constexpr int kMaxDepth = 12;
+constexpr int kInFlight = 44 * 1024;  // copy bytes kept in flight per workgroup (measured best)
 constexpr uint32_t kBufferDword3 = 0x00020000u;
 constexpr uint32_t kOob = 0x80000000u;
 
@@ -74,14 +75,17 @@ struct Layout {
     static constexpr int kSlotBytes = kCopies * kCopyBytes;
     static constexpr int kAOff = kWCopies * kCopyBytes;
     static constexpr int kSOff = kAOff + kACopies * kCopyBytes;
-    static constexpr int kDepth = std::min(kMaxDepth, kRingBudget / kSlotBytes);
+    // enough slots for about kInFlight bytes of copies ahead of the math (deeper
+    // rings measured slower), at least three, within the LDS budget
+    static constexpr int kDepth =
+        std::max(3, std::min({kMaxDepth, kRingBudget / kSlotBytes, 1 + kInFlight / kSlotBytes}));
     static constexpr int kBlocksPerWave = kChunkBlocks / GB;
     static constexpr int kVals = WORDS == 2 ? 2 : 4;           // f64 accumulators per lane and tile pair
     static constexpr int kAccBytes = RT * kAT * kVals * 64 * 8; // one wave's accumulators
     static constexpr int kLdsBytes = std::max(kDepth * kSlotBytes, (W / 2) * kAccBytes);
     static_assert(TT % GA == 0 && kChunkBlocks % GB == 0 && (GB & (GB - 1)) == 0, "wave split");
     static_assert(W <= 16, "at most 1024 threads");
-    static_assert(kDepth >= 3, "the ring needs at least three slots");
+    static_assert(kRingBudget / kSlotBytes >= 3, "the ring needs at least three slots");
     static_assert(kPerWave * (kDepth - 2) <= 63, "outstanding copies exceed the vmcnt range");
     static_assert(RT * TT * kVals * 64 * 8 <= kLdsBytes, "room for the totals");
 };
