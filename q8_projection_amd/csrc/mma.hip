@@ -47,7 +47,7 @@ constexpr int kRowGranules = kRowChunk / 16;               // 17
 constexpr int kActChunk = kChunkBlocks * kBlock;           // 256 activation bytes per row and word
 constexpr int kTileBytes = 16 * kActChunk;                 // one 16-column activation tile
 constexpr int kCopyBytes = 1024;                           // one copy instruction: 64 lanes x 16 B
-constexpr int kRingBudget = 144 * 1024;
+constexpr int kRingBudget = 156 * 1024;  // LDS for the ring (gfx950: 160 KB per workgroup)
 constexpr int kMaxDepth = 12;
 constexpr int kInFlight = 44 * 1024;  // copy bytes kept in flight per workgroup (measured best)
 constexpr uint32_t kBufferDword3 = 0x00020000u;
@@ -404,27 +404,24 @@ hipError_t run(const MmaArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Wave split per activation-tile count: one tile, eight block groups; two
-// tiles, one per wave, four block groups; four or eight tiles, four activation
-// groups by four block groups (sixteen waves).
+// Wave split per activation-tile count (measured): one tile, eight block
+// groups; two tiles, one per wave, four block groups; four tiles, two per
+// wave, eight block groups; eight tiles, two per wave, four block groups.
 template <int WORDS, int TT>
 hipError_t by_rt(int rt, const MmaArgs &a, hipStream_t s) {
-    constexpr int GA = TT == 1 ? 1 : TT == 2 ? 2 : 4;
-    constexpr int GB = TT == 1 ? 8 : 4;
+    constexpr int GA = TT <= 4 ? (TT == 1 ? 1 : 2) : 4;
+    constexpr int GB = TT == 1 ? 8 : TT == 4 ? 8 : 4;
     if (rt == 1) return run<1, TT, WORDS, GA, GB>(a, s);
     if (rt == 2) return run<2, TT, WORDS, GA, GB>(a, s);
-    if constexpr (TT * WORDS <= 4) return run<4, TT, WORDS, GA, GB>(a, s);
-    return hipErrorInvalidValue;
+    return run<4, TT, WORDS, GA, GB>(a, s);
 }
 
-// Activation tiles a stack needs, and the widest weight range (in 16-row tiles)
-// a workgroup may own with that many tiles.
+// Activation tiles a stack needs.
 int act_tiles(int words, int rows) {
     const int per = 16 / words;
     const int t = (rows + per - 1) / per;
     return t <= 1 ? 1 : t <= 2 ? 2 : t <= 4 ? 4 : 8;
 }
-int max_row_tiles(int words, int at) { return at * words <= 4 ? 4 : 2; }
 
 }  // namespace
 
@@ -432,6 +429,9 @@ bool mma_supports(int mode, int64_t n, int64_t k, int rows, const void *w, const
                   const void *scale) {
     if (mode != 1 && mode != 2) return false;
     if (rows < 2 || rows > 64 || k % (kChunkBlocks * kBlock) != 0) return false;
+    // Measured crossover with the GEMV: it is faster for two rows, and for three
+    // when the matrix is so short that a workgroup would own a single 16-row tile.
+    if (rows == 2 || (rows == 3 && n <= 16 * static_cast<int64_t>(device_info().cus))) return false;
     if (n * (k / kBlock) * kBlockBytes > (int64_t(1) << 30)) return false;
     const auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     if (!al16(w) || !al16(hi) || !al16(scale) || (mode == 2 && !al16(lo))) return false;
@@ -446,7 +446,7 @@ hipError_t launch_mma(int mode, const uint8_t *w, int64_t n, int64_t k, int rows
     const int at = act_tiles(words, rows);
     const int cus = std::max(1, device_info().cus);
     int64_t per_wg = (n + cus - 1) / cus;
-    per_wg = std::min<int64_t>(per_wg, 16 * max_row_tiles(words, at));
+    per_wg = std::min<int64_t>(per_wg, 64);
     const int rt = per_wg <= 16 ? 1 : per_wg <= 32 ? 2 : 4;
     MmaArgs a;
     a.w = w;

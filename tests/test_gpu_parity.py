@@ -205,10 +205,11 @@ def test_ragged_shapes(mode, n, k, rows):
 def test_stack_rows_equal_single_rows():
     """A row's result does not depend on the rest of its stack.  f32 mode (the
     GEMV family at every stack height): a stacked row equals that row alone.
-    Integer modes (the MFMA family serves 2..64 rows, with one summation order
-    per output whatever the stack): a row of an 8-row stack equals the same row
-    in a 2-row and in a 64-row stack.  Rows of a stack are within the gate of
-    the same row projected alone by the GEMV (different summation order)."""
+    Integer modes (the MFMA family serves 4..64 rows here, with one summation
+    order per output whatever the stack): a row of an 8-row stack equals the
+    same row in a 4-row and in a 64-row stack.  Rows of a stack are within the
+    gate of the same row projected alone by the GEMV (different summation
+    order)."""
     n, k = 515, 4096
     say("stack vs single rows", n, k)
     w = synth.weights(n, k, seed=501)
@@ -225,11 +226,11 @@ def test_stack_rows_equal_single_rows():
         hi, lo, sc = q8.quantize_act(mode, to_dev(x64))
         ys64 = q8.matmul_rows(mode, wd, n, k, hi=hi, lo=lo, scale=sc)
         ys8 = q8.matmul_rows(mode, wd, n, k, hi=hi[:8], lo=None if lo is None else lo[:8], scale=sc[:8])
-        for r0 in range(0, 8, 2):
-            ys2 = q8.matmul_rows(mode, wd, n, k, hi=hi[r0:r0 + 2], lo=None if lo is None else lo[r0:r0 + 2],
-                                 scale=sc[r0:r0 + 2])
+        for r0 in range(0, 8, 4):
+            ys4 = q8.matmul_rows(mode, wd, n, k, hi=hi[r0:r0 + 4], lo=None if lo is None else lo[r0:r0 + 4],
+                                 scale=sc[r0:r0 + 4])
             torch.cuda.synchronize()
-            assert torch.equal(ys8[r0:r0 + 2], ys2), (mode, r0)
+            assert torch.equal(ys8[r0:r0 + 4], ys4), (mode, r0)
         torch.cuda.synchronize()
         assert torch.equal(ys64[:8], ys8), mode
         ohi, olo, osc = oracle.quantize_act(mode, x64[:8])
