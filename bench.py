@@ -119,6 +119,35 @@ class Prepared:
                            residual=self.res, out=self.y)
 
 
+def sweep(spec: str, dev):
+    """Kernel time of one projection per stack height (rows 1..64) through the
+    library's own dispatch: "N,K,MODE", e.g. "14336,4096,i8x2".  Prints one JSON
+    line per height."""
+    import dataclasses
+    import torch
+    from synth import workloads as wl
+    n, k, mode = spec.split(",")
+    base = wl.Call(f"sweep_{n}x{k}_{mode}", int(n), int(k), 64, mode, "matmul_rows", w_seed=900, x_seed=901)
+    p = Prepared(base, dev)
+    p.quantize()
+    for rows in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64):
+        call = dataclasses.replace(base, rows=rows)
+
+        def launch(i, rows=rows):
+            import q8_projection_amd as q8
+            lo = None if p.lo is None else p.lo[:rows]
+            q8.matmul_rows(mode, p.w[i % p.copies], call.n, call.k, hi=p.hi[:rows], lo=lo, scale=p.sc[:rows],
+                           out=p.y[:rows])
+
+        reps = 20
+        g = capture(lambda: [launch(i) for i in range(reps)])
+        t = time_graph(g, 5) / reps
+        print(json.dumps({"sweep": f"{n}x{k}", "mode": mode, "rows": rows, "project_us": round(t * 1e6, 3),
+                          "GBps": round(call.weight_bytes / t / 1e9, 1),
+                          "pct_hbm_peak": round(call.weight_bytes / t / 1e9 / HBM_PEAK_GBPS * 100, 1),
+                          "rows_GFLOPs": round(call.flops / t / 1e9, 1)}), flush=True)
+
+
 def capture(fn, reps=1):
     import torch
     g = torch.cuda.CUDAGraph()
@@ -204,6 +233,8 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None, help="run only the named call eagerly (for profilers)")
+    ap.add_argument("--sweep", default=None, metavar="N,K,MODE",
+                    help="time one projection shape at stack heights 1..64 instead of the step")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="with --only: also run torch's device copy of this many MiB, 4 times (the "
                          "known-size reference for HBM byte counters)")
@@ -220,6 +251,9 @@ def main(argv=None):
     q8.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep:
+        sweep(args.sweep, dev)
+        return 0
     calls = step_calls()
     copies = 2  # the step graphs alternate two copies of every matrix
     prepared = [Prepared(c, dev) for c in calls]
