@@ -111,7 +111,16 @@ q8_status q8_quantize_act(int mode, const float *x, int64_t rows, int64_t k, int
  *   hi, lo, scale : the row quantized by q8_quantize_act (integer modes;
  *                 hi/lo 16-byte aligned, lo only for Q8_ACT_I8X2); NULL in
  *                 Q8_ACT_F32.
- *   x           : f32 [k], 16-byte aligned, Q8_ACT_F32 only (NULL otherwise).
+ *   x           : f32 [k], 16-byte aligned.  Required in Q8_ACT_F32.  In an
+ *                 integer mode, passing x with hi, lo and scale all NULL
+ *                 quantizes the row inside the projection (the activation
+ *                 quantization fused into its consumer; codegen_cuda::lane
+ *                 page, Modules, kernels: fused forms): the result is bit for
+ *                 bit that of q8_quantize_act then this call, and the
+ *                 quantized row is not written out.  Every workgroup quantizes
+ *                 the whole row again, so this pays off for small k (an LM
+ *                 head) and costs time for large k.  A partial set of hi, lo,
+ *                 scale is Q8_E_NULL.
  *   residual    : f32 [n] added to the result, or NULL.  4-byte aligned.
  *   y           : out, f32 [n], 4-byte aligned.  May be exactly `residual`
  *                 (in-place add); must not otherwise overlap any input.
@@ -125,7 +134,9 @@ q8_status q8_matvec(int mode, const void *w, int64_t n, int64_t k, const int8_t 
  * prefill; codegen_cuda::lane page, description: chunks of 2, 4, ... rows).
  * Arguments as q8_matvec with [rows][...] stacks: hi/lo/x [rows][k],
  * scale [rows][k/32], residual and y [rows][n].  rows >= 1; stacks wider than
- * 64 rows are run as consecutive 64-row slices.
+ * 64 rows are run as consecutive 64-row slices.  An integer-mode stack given
+ * as x (hi, lo, scale NULL) is quantized inside the projection as in
+ * q8_matvec; such calls run on the GEMV kernels, eight rows at a time.
  * Errors: Q8_E_NULL, Q8_E_SHAPE, Q8_E_ALIGN, Q8_E_MODE, Q8_E_ALIAS, Q8_E_HIP. */
 q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
                          const int8_t *lo, const float *scale, const float *x, const float *residual,

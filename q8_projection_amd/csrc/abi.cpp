@@ -48,7 +48,10 @@ q8_status check_projection(int mode, const void *w, int64_t n, int64_t k, int64_
     const int64_t nb = k / 32;
     if (n > kMaxBlocks / nb || rows * n > kMaxRowsTimesN || rows > kMaxRowsTimesN / 64) return Q8_E_SHAPE;
     if (!w || !out) return Q8_E_NULL;
-    if (mode == Q8_ACT_F32) {
+    // Integer modes take the quantized stack (hi, lo, scale) or, with all three
+    // null, the f32 stack x to quantize inside the projection.
+    const bool quantize_inside = mode != Q8_ACT_F32 && f32_allowed && !hi && !lo && !scale && x;
+    if (mode == Q8_ACT_F32 || quantize_inside) {
         if (!x) return Q8_E_NULL;
     } else {
         if (!hi || (need_scale && !scale)) return Q8_E_NULL;
@@ -56,7 +59,7 @@ q8_status check_projection(int mode, const void *w, int64_t n, int64_t k, int64_
     }
     if (!aligned(w, 4) || !aligned(out, 4)) return Q8_E_ALIGN;
     if (residual && !aligned(residual, 4)) return Q8_E_ALIGN;
-    if (mode == Q8_ACT_F32) {
+    if (mode == Q8_ACT_F32 || quantize_inside) {
         if (!aligned(x, 16)) return Q8_E_ALIGN;
     } else {
         if (!aligned(hi, 16) || (need_scale && !aligned(scale, 4))) return Q8_E_ALIGN;
@@ -65,7 +68,7 @@ q8_status check_projection(int mode, const void *w, int64_t n, int64_t k, int64_
     const int64_t wbytes = n * nb * 34;
     const int64_t abytes = rows * k;
     if (overlap(out, out_bytes, w, wbytes)) return Q8_E_ALIAS;
-    if (mode == Q8_ACT_F32) {
+    if (mode == Q8_ACT_F32 || quantize_inside) {
         if (overlap(out, out_bytes, x, abytes * 4)) return Q8_E_ALIAS;
     } else {
         if (overlap(out, out_bytes, hi, abytes)) return Q8_E_ALIAS;
@@ -145,14 +148,15 @@ q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t 
     // 64-row slices, each reading every weight block once.
     for (int64_t r0 = 0; r0 < rows; r0 += 64) {
         const int r = static_cast<int>(std::min<int64_t>(64, rows - r0));
-        const int8_t *shi = mode == Q8_ACT_F32 ? nullptr : hi + r0 * k;
-        const int8_t *slo = mode == Q8_ACT_I8X2 ? lo + r0 * k : nullptr;
-        const float *ssc = mode == Q8_ACT_F32 ? nullptr : scale + r0 * nb;
-        const float *sx = mode == Q8_ACT_F32 ? x + r0 * k : nullptr;
+        const bool inside = mode != Q8_ACT_F32 && !hi;  // validated: x given, quantized in the kernel
+        const int8_t *shi = (mode == Q8_ACT_F32 || inside) ? nullptr : hi + r0 * k;
+        const int8_t *slo = (mode == Q8_ACT_I8X2 && !inside) ? lo + r0 * k : nullptr;
+        const float *ssc = (mode == Q8_ACT_F32 || inside) ? nullptr : scale + r0 * nb;
+        const float *sx = (mode == Q8_ACT_F32 || inside) ? x + r0 * k : nullptr;
         const float *sres = residual ? residual + r0 * n : nullptr;
         float *sy = y + r0 * n;
         hipError_t e;
-        if (q8::mma_supports(mode, n, k, r, wb, shi, slo, ssc)) {
+        if (!inside && q8::mma_supports(mode, n, k, r, wb, shi, slo, ssc)) {
             e = q8::launch_mma(mode, wb, n, k, r, shi, slo, ssc, sres, sy, n, st);
         } else {
             // the GEMV family, 8 rows at a time

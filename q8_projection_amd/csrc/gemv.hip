@@ -26,6 +26,7 @@
 // v_dot4; every block term is accumulated in f64 and each output is rounded once.
 #include <algorithm>
 
+#include "actquant.h"
 #include "device.h"
 #include "launch.h"
 
@@ -118,6 +119,9 @@ __device__ __forceinline__ void dma_rows4(float *dst, int dst_stride, const floa
 template <int N>
 __device__ __forceinline__ void staged_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    // LDS stores of a stack quantized in place complete first (every copy is
+    // inline assembly the compiler does not see, so this waits on LDS only)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     // s_waitcnt fields (gfx9): vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]
     __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | 0x70 | 0xf00);
     workgroup_barrier_acquire_lds();
@@ -132,6 +136,36 @@ __device__ __forceinline__ void stage_int(const GemvArgs &a, uint8_t *lds, int t
         dma_rows16(lds + R * a.kt, a.kt, reinterpret_cast<const uint8_t *>(a.lo) + kt0, a.k, R, ktc, wave, lane);
     dma_rows4(reinterpret_cast<float *>(lds + WORDS * R * a.kt), a.kt / kBlock, a.scale + kt0 / kBlock, a.nb, R,
               ktc / kBlock, wave, lane);
+}
+
+// Integer modes with the stack given as f32 x: each workgroup quantizes the
+// tile itself into the layout stage_int copies (the lane's activation
+// quantization fused into its consumer; codegen_cuda::lane page, Modules,
+// kernels: fused forms), bit for bit as the stand-alone quantizer does.  Eight
+// lanes per 32-value block; a whole wave always takes part in a block's maximum.
+template <int R, int WORDS>
+__device__ __forceinline__ void stage_quant(const GemvArgs &a, uint8_t *lds, int ti) {
+    const int kt0 = ti * a.kt, ktc = min(a.kt, a.k - kt0);
+    const int nbt = ktc / kBlock;
+    int8_t *lhi = reinterpret_cast<int8_t *>(lds);
+    int8_t *llo = lhi + R * a.kt;
+    float *ls = reinterpret_cast<float *>(lhi + WORDS * R * a.kt);
+    const int total = R * nbt * kQuantLanes;
+    for (int t0 = 0; t0 < total; t0 += kThreads) {
+        const int t = t0 + threadIdx.x;
+        const bool valid = t < total;
+        const int blk = t / kQuantLanes, part = t % kQuantLanes;
+        const int r = blk / nbt, b = blk - r * nbt;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (valid) v = *reinterpret_cast<const float4 *>(a.x + static_cast<int64_t>(r) * a.k + kt0 + b * kBlock + 4 * part);
+        uint32_t h4, l4;
+        const float sc = quantize4<WORDS>(v, h4, l4);
+        if (valid) {
+            *reinterpret_cast<uint32_t *>(lhi + r * a.kt + b * kBlock + 4 * part) = h4;
+            if (WORDS == 2) *reinterpret_cast<uint32_t *>(llo + r * a.kt + b * kBlock + 4 * part) = l4;
+            if (part == 0) ls[r * (a.kt / kBlock) + b] = sc;
+        }
+    }
 }
 
 // f32 mode.  LDS: x [R][kt] f32.
@@ -273,6 +307,8 @@ template <int R, int WORDS>
 __device__ __forceinline__ void stage_tile(const GemvArgs &a, uint8_t *lds, int ti, int wave, int lane) {
     if constexpr (WORDS == 0)
         stage_f32<R>(a, lds, ti, wave, lane);
+    else if (a.x)
+        stage_quant<R, WORDS>(a, lds, ti);
     else
         stage_int<R, WORDS>(a, lds, ti, wave, lane);
 }
@@ -501,14 +537,19 @@ __global__ __launch_bounds__(kThreads) void gemv_ring_kernel(GemvArgs a) {
     };
 
     // Prologue: stage the stack, put the first P items in flight, barrier once
-    // the stack has landed.
-    stage_tile<R, WORDS>(a, lds, 0, wave, lane);
+    // the stack has landed.  A stack quantized here goes after the first copies
+    // (its x loads are waited for by count, which then covers the copies too, so
+    // the two latencies overlap); a copied stack goes first, so that the
+    // barrier's wait, which leaves the item copies in flight, covers it.
     Cursor ahead{0, 0};
+    const bool quantize_here = WORDS != 0 && a.x != nullptr;
+    if (!quantize_here) stage_tile<R, WORDS>(a, lds, 0, wave, lane);
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         copy_item<MR>(ws, item_base(ahead), item_len(ahead), lane, ring_lds + p * MR * kSlotBytes);
         ahead.next(ub);
     }
+    if (quantize_here) stage_tile<R, WORDS>(a, lds, 0, wave, lane);
     staged_barrier<P * MR * kCopiesPerItemRow>();
 
     double acc[MR][R];

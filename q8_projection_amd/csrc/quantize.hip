@@ -7,6 +7,7 @@
 // description).  Rounding is decided exactly as written: correctly rounded f32
 // division, round half away from zero, a fused multiply-add for the two-word
 // residual, and no other contraction.
+#include "actquant.h"
 #include "device.h"
 #include "launch.h"
 
@@ -16,25 +17,7 @@ namespace q8 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kLanesPerBlock = 8;  // 8 lanes x 4 values = one 32-value block
-
-__device__ __forceinline__ int quant_clamped(float v) {
-    float r = roundf(v);  // half away from zero
-    r = r > 127.0f ? 127.0f : r;
-    r = r < -127.0f ? -127.0f : r;
-    return static_cast<int>(r);
-}
-
-__device__ __forceinline__ float group_max8(float v) {
-#pragma unroll
-    for (int off = 1; off < kLanesPerBlock; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
-__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
-    return (static_cast<uint32_t>(a) & 0xffu) | ((static_cast<uint32_t>(b) & 0xffu) << 8) |
-           ((static_cast<uint32_t>(c) & 0xffu) << 16) | ((static_cast<uint32_t>(d) & 0xffu) << 24);
-}
+constexpr int kLanesPerBlock = kQuantLanes;  // 8 lanes x 4 values = one 32-value block
 
 // One thread per 4 consecutive values; 8 threads per 32-value block.  x, hi and
 // lo are contiguous [rows][k] with k a multiple of 32, so block t/8 covers values
@@ -49,22 +32,11 @@ __global__ __launch_bounds__(kThreads) void quantize_act_kernel(const float *__r
     const bool valid = blk < nblocks;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (valid) v = *reinterpret_cast<const float4 *>(x + t * 4);
-    float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    amax = group_max8(amax);
+    uint32_t h4, l4;
+    const float s = quantize4<WORDS>(v, h4, l4);  // all 8 lanes of the block take part
     if (!valid) return;
-    const float s = amax / 127.0f;
-    const float vals[4] = {v.x, v.y, v.z, v.w};
-    int h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        h[i] = (s == 0.0f) ? 0 : quant_clamped(vals[i] / s);
-        if (WORDS == 2) {
-            const float resid = __builtin_fmaf(-s, static_cast<float>(h[i]), vals[i]);
-            l[i] = (s == 0.0f) ? 0 : quant_clamped((resid * 128.0f) / s);
-        }
-    }
-    *reinterpret_cast<uint32_t *>(hi + t * 4) = pack4(h[0], h[1], h[2], h[3]);
-    if (WORDS == 2) *reinterpret_cast<uint32_t *>(lo + t * 4) = pack4(l[0], l[1], l[2], l[3]);
+    *reinterpret_cast<uint32_t *>(hi + t * 4) = h4;
+    if (WORDS == 2) *reinterpret_cast<uint32_t *>(lo + t * 4) = l4;
     if ((t % kLanesPerBlock) == 0) scale[blk] = s;
 }
 

@@ -94,6 +94,13 @@ def test_null_pointers():
     assert _mv(scale=None) == NULL
     assert _mv(mode=2, lo=None) == NULL
     assert _mv(mode=0, hi=None, lo=None, scale=None, x=None) == NULL
+    # integer modes: the quantized stack, or x alone; a partial set is an error
+    assert _mv(mode=2, hi=None, lo=None, scale=None, x=None) == NULL
+    assert _mv(mode=2, hi=None, x=BASE + 96 * MB) == NULL                  # lo and scale still given
+    assert _mv(mode=1, hi=None, lo=None, x=BASE + 96 * MB) == NULL         # scale still given
+    assert _mm(mode=1, hi=BASE + 16 * MB, lo=None, scale=None, x=BASE + 96 * MB) == NULL
+    # block sums never quantize: hi is required
+    assert q8.lib().q8_block_sums(1, BASE, 4, 256, 1, None, None, BASE + 2 * MB, None) == NULL
     assert q8.lib().q8_quantize_act(2, BASE, 1, 256, BASE + MB, None, BASE + 2 * MB, None) == NULL
     assert q8.lib().q8_quantize_act(1, None, 1, 256, BASE + MB, None, BASE + 2 * MB, None) == NULL
     assert q8.lib().q8_quantize_weights(None, 4, 256, BASE + MB, None) == NULL
@@ -107,6 +114,7 @@ def test_alignment():
     assert _mv(y=BASE + 64 * MB + 1) == ALIGN
     assert _mv(residual=BASE + 80 * MB + 2) == ALIGN
     assert _mv(mode=0, hi=None, lo=None, scale=None, x=BASE + 96 * MB + 4) == ALIGN
+    assert _mv(mode=2, hi=None, lo=None, scale=None, x=BASE + 96 * MB + 8) == ALIGN
     assert q8.lib().q8_quantize_act(1, BASE + 4, 1, 256, BASE + MB, None, BASE + 2 * MB, None) == ALIGN
     assert q8.lib().q8_quantize_weights(BASE + 2, 4, 256, BASE + MB, None) == ALIGN
 
@@ -119,6 +127,8 @@ def test_aliasing():
     assert _mv(y=BASE + 32 * MB) == ALIAS                       # on lo
     assert _mv(y=BASE + 48 * MB + 4) == ALIAS                   # inside scale
     assert _mv(mode=0, hi=None, lo=None, scale=None, x=BASE + 64 * MB - 256) == ALIAS
+    assert _mv(mode=1, hi=None, lo=None, scale=None, x=BASE + 64 * MB - 256) == ALIAS
+    assert _mm(mode=2, hi=None, lo=None, scale=None, x=BASE + 64 * MB - 4 * 256) == ALIAS
     r = BASE + 80 * MB
     assert _mv(residual=r, y=r + 4) == ALIAS                    # partial overlap with residual
     assert q8.lib().q8_quantize_act(2, BASE, 1, 256, BASE + 512, BASE + 2048, BASE + 4096, None) == ALIAS

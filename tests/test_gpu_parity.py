@@ -241,6 +241,40 @@ def test_stack_rows_equal_single_rows():
         gate(one.cpu().numpy(), r[3], a[3], f"single {mode}")
 
 
+@pytest.mark.parametrize("mode", ["i8", "i8x2"])
+@pytest.mark.parametrize("n,k,rows", [(5000, 2048, 1), (4096, 14336, 1), (700, 1088, 1), (1000, 4096, 3),
+                                      (999, 2048, 8), (300, 512, 13)])
+def test_quantization_inside_the_projection_is_bitwise_the_same(mode, n, k, rows):
+    """An integer-mode stack given as f32 x is quantized inside the projection
+    (fused into its consumer) with the same bits as q8_quantize_act followed by
+    the projection, whatever kernel runs it."""
+    say("quantize inside", mode, n, k, rows)
+    w = synth.weights(n, k, seed=1400 + n)
+    x = synth.activations(rows, k, seed=1500 + k, outlier_frac=0.02)
+    res = synth.normal(1600 + rows, (rows, n))
+    wd = to_dev(oracle.quantize_weights(w))
+    xd, rd = to_dev(x), to_dev(res)
+    hi, lo, sc = q8.quantize_act(mode, xd)
+    separate = q8.matmul_rows(mode, wd, n, k, hi=hi, lo=lo, scale=sc, residual=rd)
+    inside = q8.matmul_rows(mode, wd, n, k, x=xd, residual=rd)
+    gemv_separate = torch.cat([q8.matmul_rows(mode, wd, n, k, hi=hi[r0:r0 + 1],
+                                              lo=None if lo is None else lo[r0:r0 + 1], scale=sc[r0:r0 + 1],
+                                              residual=rd[r0:r0 + 1]) for r0 in range(rows)])
+    inside_rows = torch.cat([q8.matmul_rows(mode, wd, n, k, x=xd[r0:r0 + 1], residual=rd[r0:r0 + 1])
+                             for r0 in range(rows)])
+    torch.cuda.synchronize()
+    # one row at a time both run the GEMV: identical bits
+    assert torch.equal(inside_rows, gemv_separate)
+    # a stack: the fused call runs the GEMV in 8-row chunks, the separate one may
+    # run the MFMA kernel (another summation order): both within the gate
+    (r, a), _ = oracle_path(workloads.Call("q", n, k, rows, mode, "matmul_rows", w_seed=0),
+                            oracle.quantize_weights(w), x, res)
+    gate(inside.cpu().numpy(), r, a, f"inside {mode} {n}x{k} rows={rows}")
+    gate(separate.cpu().numpy(), r, a, f"separate {mode} {n}x{k} rows={rows}")
+    if rows <= 2:
+        assert torch.equal(inside, separate)
+
+
 def test_inplace_residual_and_adjacent_buffers():
     n, k, rows = 1000, 2048, 4
     say("in-place residual", n, k, rows)
