@@ -142,6 +142,33 @@ q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t 
                          const int8_t *lo, const float *scale, const float *x, const float *residual,
                          float *y, void *stream);
 
+/* y = W x (+ residual) for one activation row, and idx = argmax_i y[i] (the
+ * lowest i among equal maxima) from the same launch: the LM head closing a
+ * decode step (model::author page, Functions: the head reads the last row
+ * only).  Arguments as q8_matvec (including x alone in an integer mode), plus:
+ *   idx       : out, int32 (device), 4-byte aligned.
+ *   workspace : device memory of q8_argmax_workspace_bytes(n) bytes, 16-byte
+ *               aligned, zero-filled by the caller before its first use.  Its
+ *               first 16 bytes hold a counter that every call leaves at zero
+ *               again; the rest is scratch.  So one workspace serves call
+ *               after call without clearing, but two calls in flight at once
+ *               must not share it.
+ * The arg-max is over the stored f32 y.  Every workgroup reduces its rows to a
+ * partial in the workspace; the last one to finish, told by an atomic counter,
+ * reduces the partials.  The order of arrival does not change the result.
+ * Limits (else Q8_E_SHAPE): 1 <= n <= 2^31 - 1, weights at most 1 GiB, and the
+ * row's staged activations within 64 KiB (k up to 30784 two-word, 58240
+ * one-word, 16384 in f32 mode).  idx and the workspace must not overlap any other
+ * argument (Q8_E_ALIAS).
+ * Errors: Q8_E_NULL, Q8_E_SHAPE, Q8_E_ALIGN, Q8_E_MODE, Q8_E_ALIAS, Q8_E_HIP. */
+q8_status q8_matvec_argmax(int mode, const void *w, int64_t n, int64_t k, const int8_t *hi, const int8_t *lo,
+                           const float *scale, const float *x, const float *residual, float *y, int32_t *idx,
+                           void *workspace, void *stream);
+
+/* Bytes of the q8_matvec_argmax workspace for n weight rows on the current
+ * device (0 if n is out of range). */
+int64_t q8_argmax_workspace_bytes(int64_t n);
+
 /* The exact int32 block dot products of the integer modes, for checking:
  *   sums[r][n][b][0] = sum_j q[n][b][j] * hi[r][32b+j]
  *   sums[r][n][b][1] = sum_j q[n][b][j] * lo[r][32b+j]   (Q8_ACT_I8X2 only)

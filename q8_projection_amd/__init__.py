@@ -35,6 +35,8 @@ SIGNATURES = {
     "q8_quantize_act": (_I, [_I, _P, _I64, _I64, _P, _P, _P, _P]),
     "q8_matvec": (_I, [_I, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "q8_matmul_rows": (_I, [_I, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "q8_matvec_argmax": (_I, [_I, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "q8_argmax_workspace_bytes": (_I64, [_I64]),
     "q8_block_sums": (_I, [_I, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "q8_status_name": (ctypes.c_char_p, [_I]),
     "q8_version": (_I, []),
@@ -153,6 +155,31 @@ def matvec(mode, w: torch.Tensor, n: int, k: int, hi=None, lo=None, scale=None, 
     _check("q8_matvec", lib().q8_matvec(m, _ptr(w), n, k, _ptr(hi), _ptr(lo), _ptr(scale), _ptr(x),
                                         _ptr(residual), _ptr(out), _stream(stream)))
     return out
+
+
+def argmax_workspace_bytes(n: int) -> int:
+    """Bytes of the matvec_argmax workspace for n weight rows."""
+    return int(lib().q8_argmax_workspace_bytes(n))
+
+
+def matvec_argmax(mode, w: torch.Tensor, n: int, k: int, hi=None, lo=None, scale=None, x=None,
+                  residual=None, out=None, idx=None, workspace=None, stream=None):
+    """(y [n], idx) with idx = argmax y (lowest index among equal maxima), one launch.
+    The workspace must start zero-filled; each call puts its counter (the first
+    16 bytes) back to zero, so a caller may keep one per stream and pass it
+    every time."""
+    m = _mode(mode)
+    dev = _device_of(w, hi, x)
+    if out is None:
+        out = torch.empty((n,), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((1,), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.zeros(max(16, argmax_workspace_bytes(n)), dtype=torch.uint8, device=dev)
+    _check("q8_matvec_argmax", lib().q8_matvec_argmax(m, _ptr(w), n, k, _ptr(hi), _ptr(lo), _ptr(scale), _ptr(x),
+                                                      _ptr(residual), _ptr(out), _ptr(idx), _ptr(workspace),
+                                                      _stream(stream)))
+    return out, idx
 
 
 def block_sums(mode, w: torch.Tensor, n: int, k: int, hi, lo=None, out=None, rows: int | None = None,

@@ -178,6 +178,42 @@ q8_status q8_matvec(int mode, const void *w, int64_t n, int64_t k, const int8_t 
     return q8_matmul_rows(mode, w, n, k, 1, hi, lo, scale, x, residual, y, stream);
 }
 
+int64_t q8_argmax_workspace_bytes(int64_t n) {
+    if (n < 1 || n > INT32_MAX) return 0;
+    return 16 + 8 * q8::gemv_row_grid(n);
+}
+
+q8_status q8_matvec_argmax(int mode, const void *w, int64_t n, int64_t k, const int8_t *hi, const int8_t *lo,
+                           const float *scale, const float *x, const float *residual, float *y, int32_t *idx,
+                           void *workspace, void *stream) {
+    if (q8_status s = check_projection(mode, w, n, k, 1, hi, lo, scale, x, residual, y, n * 4, true, true);
+        s != Q8_OK)
+        return s;
+    if (n < 1 || n > INT32_MAX) return Q8_E_SHAPE;
+    // one launch: the weights in one buffer and the stack resident in LDS
+    if (n * (k / 32) * 34 > (int64_t(1) << 30) || !q8::gemv_row_resident(mode, k)) return Q8_E_SHAPE;
+    if (!idx || !workspace) return Q8_E_NULL;
+    if (!aligned(idx, 4) || !aligned(workspace, 16)) return Q8_E_ALIGN;
+    const int64_t wsb = q8_argmax_workspace_bytes(n);
+    const int64_t wbytes = n * (k / 32) * 34;
+    const bool inside = mode != Q8_ACT_F32 && !hi;
+    const void *ins[] = {w, hi, lo, scale, x, residual, y};
+    const int64_t in_bytes[] = {wbytes, (mode == Q8_ACT_F32 || inside) ? 0 : k, (mode == Q8_ACT_I8X2 && !inside) ? k : 0,
+                                (mode == Q8_ACT_F32 || inside) ? 0 : (k / 32) * 4, (mode == Q8_ACT_F32 || inside) ? k * 4 : 0,
+                                residual ? n * 4 : 0, n * 4};
+    for (int i = 0; i < 7; ++i)
+        if (ins[i] && in_bytes[i] > 0 && (overlap(idx, 4, ins[i], in_bytes[i]) || overlap(workspace, wsb, ins[i], in_bytes[i])))
+            return Q8_E_ALIAS;
+    if (overlap(idx, 4, workspace, wsb)) return Q8_E_ALIAS;
+    const hipError_t e = q8::launch_gemv(mode, static_cast<const uint8_t *>(w), n, k, 1,
+                                         (mode == Q8_ACT_F32 || inside) ? nullptr : hi,
+                                         (mode == Q8_ACT_I8X2 && !inside) ? lo : nullptr,
+                                         (mode == Q8_ACT_F32 || inside) ? nullptr : scale,
+                                         (mode == Q8_ACT_F32 || inside) ? x : nullptr, residual, y, as_stream(stream),
+                                         idx, workspace);
+    return from_hip(e);
+}
+
 q8_status q8_block_sums(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
                         const int8_t *lo, int32_t *sums, void *stream) {
     const int words = mode == Q8_ACT_I8X2 ? 2 : 1;

@@ -62,6 +62,8 @@ struct GemvArgs {
     int ntiles;
     int ub;                 // 64-block columns per tile
     int64_t num_groups;     // row groups of MR rows
+    int32_t *argmax;        // one activation row: also write the arg-max of y here, or null
+    uint32_t *argmax_work;  // its workspace: [0] a counter left at zero, then [grid][2] partials
 };
 
 // ------------------------------------------------------------------ staging
@@ -314,10 +316,120 @@ __device__ __forceinline__ void stage_tile(const GemvArgs &a, uint8_t *lds, int 
 }
 
 // Output element (r, row): the f64 total plus the residual in f64, rounded once.
-__device__ __forceinline__ void write_output(const GemvArgs &a, int r, int64_t row, double tot) {
+__device__ __forceinline__ float write_output(const GemvArgs &a, int r, int64_t row, double tot) {
     const int64_t o = static_cast<int64_t>(r) * a.ldy + row;
     const double res = a.residual ? static_cast<double>(a.residual[o]) : 0.0;
-    a.y[o] = static_cast<float>(tot + res);
+    const float v = static_cast<float>(tot + res);
+    a.y[o] = v;
+    return v;
+}
+
+// ----------------------------------------------------------------- arg-max
+
+// The LM head closes a decode step by picking the next token (model::author
+// page, Functions: the head reads the last row only): argmax_i y[i], the
+// lowest i among equal maxima.  Fused into the GEMV epilogue: every workgroup
+// reduces its rows to one (value, row) partial in the workspace; an agent-scope
+// atomic counter tells the last workgroup to finish, which reduces the partials
+// (a max with a fixed tie-break, so the order of arrival does not matter),
+// writes the index and puts the counter back to zero for the next call.
+__device__ __forceinline__ bool argmax_better(float v, int32_t i, float bv, int32_t bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ void argmax_wave(float &v, int32_t &i) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(v, off, 64);
+        const int32_t oi = __shfl_xor(i, off, 64);
+        if (argmax_better(ov, oi, v, i)) {
+            v = ov;
+            i = oi;
+        }
+    }
+}
+
+// Called by every thread of the workgroup, with this lane's best (value, row).
+__device__ __forceinline__ void argmax_finish(const GemvArgs &a, float v, int32_t i, int wave, int lane) {
+    __shared__ float wave_v[kWaves];
+    __shared__ int32_t wave_i[kWaves];
+    __shared__ int is_last;
+    uint32_t *counter = a.argmax_work;
+    uint32_t *part = a.argmax_work + 4;  // 16-byte header, then [grid][2]
+    argmax_wave(v, i);
+    if (lane == 0) {
+        wave_v[wave] = v;
+        wave_i[wave] = i;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float bv = wave_v[0];
+        int32_t bi = wave_i[0];
+        for (int w = 1; w < kWaves; ++w)
+            if (argmax_better(wave_v[w], wave_i[w], bv, bi)) {
+                bv = wave_v[w];
+                bi = wave_i[w];
+            }
+        part[2 * blockIdx.x] = __float_as_uint(bv);
+        part[2 * blockIdx.x + 1] = static_cast<uint32_t>(bi);
+        // release: the partial is visible before the count; acquire: so is every earlier one
+        const uint32_t done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = done == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!is_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    v = -__builtin_inff();
+    i = INT32_MAX;
+    for (uint32_t b = threadIdx.x; b < gridDim.x; b += blockDim.x) {
+        const float pv = __uint_as_float(part[2 * b]);
+        const int32_t pi = static_cast<int32_t>(part[2 * b + 1]);
+        if (argmax_better(pv, pi, v, i)) {
+            v = pv;
+            i = pi;
+        }
+    }
+    argmax_wave(v, i);
+    __syncthreads();  // every wave has read wave_v/wave_i of the first round
+    if (lane == 0) {
+        wave_v[wave] = v;
+        wave_i[wave] = i;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float bv = wave_v[0];
+        int32_t bi = wave_i[0];
+        for (int w = 1; w < kWaves; ++w)
+            if (argmax_better(wave_v[w], wave_i[w], bv, bi)) {
+                bv = wave_v[w];
+                bi = wave_i[w];
+            }
+        *a.argmax = bi;
+        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+    }
+}
+
+// Epilogue of the resident kernels: scale (1/128 in two-word mode, exact),
+// residual, one rounding, store; then the arg-max if asked for (one row).
+template <int R, int WORDS, int MR>
+__device__ __forceinline__ void finish_rows(const GemvArgs &a, const double *totals, int G, int64_t gw,
+                                            int64_t stride, int wave, int lane) {
+    const double post = WORDS == 2 ? 1.0 / 128.0 : 1.0;
+    float best = -__builtin_inff();
+    int32_t best_row = INT32_MAX;
+    for (int i = lane; i < G * MR * R; i += 64) {
+        const int gi = i / (MR * R), m = (i / R) % MR, r = i % R;
+        const int64_t row = (gw + static_cast<int64_t>(gi) * stride) * MR + m;
+        if (row < a.n) {
+            const float v = write_output(a, r, row, totals[i] * post);
+            if (argmax_better(v, static_cast<int32_t>(row), best, best_row)) {
+                best = v;
+                best_row = static_cast<int32_t>(row);
+            }
+        }
+    }
+    if constexpr (R == 1 && MR == 1)
+        if (a.argmax) argmax_finish(a, best, best_row, wave, lane);
 }
 
 __host__ __device__ inline size_t stack_bytes(int rows, int words, int kt) {
@@ -434,14 +546,8 @@ __global__ __launch_bounds__(kThreads) void gemv_resident_kernel(GemvArgs a) {
             cur.next(ub);
         }
     }
-    // Epilogue: scale (1/128 in two-word mode, exact), residual, one rounding.
-    const double post = WORDS == 2 ? 1.0 / 128.0 : 1.0;
     wave_lds_sync();  // lane 0 parked the totals the whole wave reads now
-    for (int i = lane; i < G * MR * R; i += 64) {
-        const int gi = i / (MR * R), m = (i / R) % MR, r = i % R;
-        const int64_t row = (gw + static_cast<int64_t>(gi) * stride) * MR + m;
-        if (row < a.n) write_output(a, r, row, totals[i] * post);
-    }
+    finish_rows<R, WORDS, MR>(a, totals, G, gw, stride, wave, lane);
 }
 
 // ---------------------------------------------------- resident kernel, LDS ring
@@ -584,13 +690,8 @@ __global__ __launch_bounds__(kThreads) void gemv_ring_kernel(GemvArgs a) {
         }
     }
     wait_vm<0>();  // the dead refills read nothing but still write the ring
-    const double post = WORDS == 2 ? 1.0 / 128.0 : 1.0;
     wave_lds_sync();  // lane 0 parked the totals the whole wave reads now
-    for (int i = lane; i < G * MR * R; i += 64) {
-        const int gi = i / (MR * R), m = (i / R) % MR, r = i % R;
-        const int64_t row = (gw + static_cast<int64_t>(gi) * stride) * MR + m;
-        if (row < a.n) write_output(a, r, row, totals[i] * post);
-    }
+    finish_rows<R, WORDS, MR>(a, totals, G, gw, stride, wave, lane);
 }
 
 // --------------------------------------------------------------- tiled kernel
@@ -721,10 +822,24 @@ hipError_t dispatch_f64(int rows, const GemvArgs &a, hipStream_t s) {
 
 }  // namespace
 
+bool gemv_row_resident(int mode, int64_t k) {
+    const int words = mode == 0 ? 0 : mode;
+    return tile_columns(static_cast<int>(k), 1, words) >= k;
+}
+
+int64_t gemv_row_grid(int64_t n) {
+    // as run<1, WORDS, 1, P> sizes the resident grid: one group per row
+    const int64_t waves = std::max<int64_t>(std::min<int64_t>(n, static_cast<int64_t>(device_info().cus) * kWavesPerCu),
+                                            (n + kOutPerWave - 1) / kOutPerWave);
+    return (waves + kWaves - 1) / kWaves;
+}
+
 hipError_t launch_gemv(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
                        const int8_t *lo, const float *scale, const float *x, const float *residual,
-                       float *y, hipStream_t stream) {
+                       float *y, hipStream_t stream, int32_t *argmax, void *argmax_work) {
     GemvArgs a{};
+    a.argmax = argmax;
+    a.argmax_work = static_cast<uint32_t *>(argmax_work);
     a.w = w;
     a.hi = hi;
     a.lo = lo;

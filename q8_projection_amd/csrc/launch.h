@@ -21,9 +21,17 @@ hipError_t launch_quantize_act(int words, const float *x, int64_t rows, int64_t 
 
 // Projection of up to 8 rows with the int8 dot4 GEMV kernels (integer modes)
 // or the f64 GEMV (f32 mode).  mode: 0 f32, 1 one-word, 2 two-word.
+// With `argmax` (one row, resident stack, one launch): also write argmax_i y[i]
+// (lowest i among equal maxima) there, using `argmax_work` (gemv_argmax_work_bytes,
+// zero-filled before its first use and left zero-filled).
 hipError_t launch_gemv(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
                        const int8_t *lo, const float *scale, const float *x, const float *residual,
-                       float *y, hipStream_t stream);
+                       float *y, hipStream_t stream, int32_t *argmax = nullptr, void *argmax_work = nullptr);
+// Workgroups of the one-row resident launch over n weight rows.
+int64_t gemv_row_grid(int64_t n);
+// Whether the one-row projection over k columns keeps its stack resident in LDS
+// (a single launch that can finish with the fused arg-max).
+bool gemv_row_resident(int mode, int64_t k);
 
 // Projection of 2..64 rows with the LDS-staged int8 MFMA kernel (integer
 // modes).  y and residual have row stride ldy.

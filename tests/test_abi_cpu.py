@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["q8_quantize_weights", "q8_quantize_act", "q8_matvec", "q8_matmul_rows",
-                            "q8_block_sums", "q8_status_name", "q8_version"])
+                            "q8_matvec_argmax", "q8_argmax_workspace_bytes", "q8_block_sums",
+                            "q8_status_name", "q8_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -133,3 +134,34 @@ def test_aliasing():
     assert _mv(residual=r, y=r + 4) == ALIAS                    # partial overlap with residual
     assert q8.lib().q8_quantize_act(2, BASE, 1, 256, BASE + 512, BASE + 2048, BASE + 4096, None) == ALIAS
     assert q8.lib().q8_quantize_act(2, BASE, 1, 256, BASE + MB, BASE + MB + 128, BASE + 2 * MB, None) == ALIAS
+
+
+def _ma(mode=1, w=BASE, n=64, k=256, hi=BASE + 16 * MB, lo=BASE + 32 * MB, scale=BASE + 48 * MB, x=None,
+        residual=None, y=BASE + 64 * MB, idx=BASE + 72 * MB, work=BASE + 76 * MB):
+    return q8.lib().q8_matvec_argmax(mode, w, n, k, hi, lo, scale, x, residual, y, idx, work, None)
+
+
+def test_argmax_workspace_size():
+    lib = q8.lib()
+    assert lib.q8_argmax_workspace_bytes(0) == 0
+    assert lib.q8_argmax_workspace_bytes(-5) == 0
+    assert lib.q8_argmax_workspace_bytes(1 << 31) == 0
+    sizes = [lib.q8_argmax_workspace_bytes(n) for n in (1, 4, 5, 100, 151936)]
+    assert all(b >= 24 and (b - 16) % 8 == 0 for b in sizes)
+    assert sizes == sorted(sizes)
+
+
+def test_argmax_validation():
+    assert _ma(idx=None) == NULL
+    assert _ma(work=None) == NULL
+    assert _ma(hi=None) == NULL                                   # lo/scale given: a partial set
+    assert _ma(idx=BASE + 72 * MB + 2) == ALIGN
+    assert _ma(work=BASE + 76 * MB + 8) == ALIGN
+    assert _ma(n=0) == SHAPE                                      # an arg-max of nothing
+    assert _ma(mode=2, k=40000) == SHAPE                          # stack beyond the resident LDS budget
+    assert _ma(mode=0, hi=None, lo=None, scale=None, x=BASE + 96 * MB, k=16448) == SHAPE
+    assert _ma(n=1 << 20, k=1 << 15) == SHAPE                     # weights over 1 GiB: not one launch
+    assert _ma(idx=BASE + 64 * MB + 8) == ALIAS                   # idx inside y
+    assert _ma(work=BASE + 16) == ALIAS                           # workspace over W
+    assert _ma(idx=BASE + 76 * MB + 16) == ALIAS                  # idx inside the workspace
+    assert _ma(mode=3) == MODE

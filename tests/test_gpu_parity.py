@@ -275,6 +275,72 @@ def test_quantization_inside_the_projection_is_bitwise_the_same(mode, n, k, rows
         assert torch.equal(inside, separate)
 
 
+@pytest.mark.parametrize("n,k,mode,with_res,inside", [(151936, 2048, "i8", False, False),
+                                                     (50000, 4096, "i8x2", True, False),
+                                                     (1000, 1088, "i8", False, False),
+                                                     (3000, 2048, "f32", True, False),
+                                                     (20000, 2048, "i8", False, True)])
+def test_argmax_fused_into_the_projection(n, k, mode, with_res, inside):
+    """One launch writes y and argmax y (the lowest index among equal maxima);
+    y is bitwise the plain projection's, the index is the first maximum of that
+    y, and the workspace's counter comes back to zero, ready for the next call."""
+    say("argmax", n, k, mode, with_res, inside)
+    w = synth.weights(n, k, seed=1700 + n % 97)
+    x = synth.activations(1, k, seed=1800 + k)[0]
+    res = synth.normal(1900, (n,)) if with_res else None
+    wd, xd = to_dev(oracle.quantize_weights(w)), to_dev(x)
+    rd = None if res is None else to_dev(res)
+    if mode == "f32":
+        args = dict(x=xd)
+    elif inside:
+        args = dict(x=xd)
+    else:
+        hi, lo, sc = q8.quantize_act(mode, xd.unsqueeze(0))
+        args = dict(hi=hi[0], lo=None if lo is None else lo[0], scale=sc[0])
+    y_ref = q8.matvec(mode, wd, n, k, residual=rd, **args)
+    work = torch.zeros(q8.argmax_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    for call in range(2):
+        y, idx = q8.matvec_argmax(mode, wd, n, k, residual=rd, workspace=work, **args)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), call
+        y_np = y.cpu().numpy()
+        assert int(idx.item()) == int(np.argmax(y_np)), call
+        assert int(work[:16].count_nonzero().item()) == 0, call
+    # the oracle agrees wherever its top two are further apart than the gate
+    if mode == "f32":
+        r, a = oracle.project(mode, oracle.quantize_weights(w), n, k, 1, x=x[None], residual=None if res is None else res[None])
+    else:
+        ohi, olo, osc = oracle.quantize_act(mode, x[None])
+        r, a = oracle.project(mode, oracle.quantize_weights(w), n, k, 1, hi=ohi, lo=olo, scale=osc,
+                              residual=None if res is None else res[None])
+    r, a = r[0], a[0]
+    top = np.argsort(r)[::-1][:2]
+    tol = 1e-5 * abs(r[top]) + 2.0 ** -40 * a[top]
+    if r[top[0]] - r[top[1]] > 2 * tol.max():
+        assert int(idx.item()) == int(top[0])
+
+
+def test_argmax_ties_go_to_the_lowest_index():
+    n, k = 4000, 2048
+    say("argmax ties", n, k)
+    w = synth.weights(n, k, seed=2001)
+    x = synth.activations(1, k, seed=2002)
+    xd = to_dev(x[0])
+    hi, lo, sc = q8.quantize_act("i8", xd.unsqueeze(0))
+    y = q8.matvec("i8", to_dev(oracle.quantize_weights(w)), n, k, hi=hi[0], scale=sc[0])
+    torch.cuda.synchronize()
+    m = int(torch.argmax(y).item())
+    low, high = m // 3, min(n - 1, m + 17 if m + 17 < n else m - 1)
+    w2 = w.copy()
+    w2[low] = w[m]      # an exact copy of the maximum row below it ...
+    w2[high] = w[m]     # ... and one above it
+    wd2 = to_dev(oracle.quantize_weights(w2))
+    y2, idx = q8.matvec_argmax("i8", wd2, n, k, hi=hi[0], scale=sc[0])
+    torch.cuda.synchronize()
+    assert float(y2[low]) == float(y2[m]) == float(y2[high]) == float(y2.max())
+    assert int(idx.item()) == min(low, m, high)
+
+
 def test_inplace_residual_and_adjacent_buffers():
     n, k, rows = 1000, 2048, 4
     say("in-place residual", n, k, rows)
