@@ -163,6 +163,33 @@ def sweep(spec: str, dev):
                           "rows_GFLOPs": round(call.flops / t / 1e9, 1)}), flush=True)
 
 
+def time_head_argmax(p, reps):
+    """Kernel time of the LM head with its arg-max fused in (not part of the
+    step); checks the index against the first maximum of the plain head's y."""
+    import torch
+    import q8_projection_amd as q8
+    c = p.call
+    p.quantize()
+    p.project(0)
+    torch.cuda.synchronize()
+    y = p.y[0].clone()
+    idx = torch.empty((1,), dtype=torch.int32, device=y.device)
+    work = torch.zeros(q8.argmax_workspace_bytes(c.n), dtype=torch.uint8, device=y.device)
+    out = torch.empty_like(y)
+
+    def launch(i):
+        q8.matvec_argmax(c.mode, p.w[i % p.copies], c.n, c.k, hi=p.hi[0], scale=p.sc[0], out=out, idx=idx,
+                         workspace=work)
+
+    g = capture(lambda: [launch(i) for i in range(reps)])
+    t = time_graph(g, 5) / reps
+    want = int(torch.nonzero(y == y.max())[0].item())
+    if not torch.equal(out, y) or int(idx.item()) != want:
+        raise RuntimeError("the LM head with a fused arg-max differs from the plain head")
+    return {"project_us": round(t * 1e6, 3), "GBps": round(c.weight_bytes / t / 1e9, 1),
+            "pct_hbm_peak": round(c.weight_bytes / t / 1e9 / HBM_PEAK_GBPS * 100, 1), "index": want}
+
+
 def capture(fn, reps=1):
     import torch
     g = torch.cuda.CUDAGraph()
@@ -342,6 +369,7 @@ def main(argv=None):
                                  "pct_hbm_peak": round(p.call.weight_bytes / tp / 1e9 / HBM_PEAK_GBPS * 100, 1),
                                  "rows_GFLOPs": round(p.call.flops / tp / 1e9, 1),
                                  "hbm_bytes_counted": stored_traffic(p.call.name)}
+    head_argmax = time_head_argmax(next(p for p in prepared if p.call.name == "lm_head"), reps)
     by_rows = {}
     for name, d in per_call.items():
         key = str(d["rows"])
@@ -384,6 +412,7 @@ def main(argv=None):
         "pct_hbm_peak": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBPS * 100, 1),
         "per_rows": per_rows,
         "per_call": per_call,
+        "lm_head_argmax": head_argmax,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -607,11 +607,90 @@ __device__ __forceinline__ void read_item(const uint8_t *slot, uint32_t lane_par
     }
 }
 
+// ------------------------------------------------- stack staged item by item
+
+// A copied stack (integer words and scales, or f32 values) is staged in parts:
+// part u holds the stack's columns [2048u, 2048u + 2048) of every row, the
+// columns of the 64-block item u.  Part u is copied just before the weights of
+// item u, so the wait for an item's weights also covers its part; in the first
+// pass over the columns the workgroup meets at a barrier before each item.  A
+// wave's first item then waits for one part rather than for the whole stack,
+// which every workgroup asks L2 for at once at the start.  The LDS row stride kt
+// is rounded up to a multiple of 2048 columns, so a part never spills into the
+// next row; lanes past k read zeros.
+constexpr int kPartCols = 64 * kBlock;  // 2048
+
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t off) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t off) {
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds) : "memory");
+}
+
+struct StackStream {
+    __amdgpu_buffer_rsrc_t hi, lo, scale;  // [R][k], [R][k], [R][nb]; f32 mode: hi covers x [R][k]
+};
+
+// Copies of one part: per row, 1 KB copies of the int8 words (two per word) and
+// one 256-byte copy of the 64 block scales, or eight 1 KB copies of f32 values.
+// They are dealt round-robin to the workgroup's waves; a share that runs past
+// the last copy repeats an earlier one (the same bytes to the same place), so
+// every wave issues kPerWave copies a part.
+template <int R, int WORDS>
+struct PartPlan {
+    static constexpr int kPerRow = WORDS == 0 ? 8 : 2 * WORDS + 1;
+    static constexpr int kCopies = R * kPerRow;
+    static constexpr int kPerWave = (kCopies + kWaves - 1) / kWaves;
+};
+
+template <int R, int WORDS>
+__device__ __forceinline__ void copy_part(const GemvArgs &a, const StackStream &ss, uint32_t stack_lds, int u,
+                                          int wave, int lane) {
+    using Plan = PartPlan<R, WORDS>;
+#pragma unroll
+    for (int i = 0; i < Plan::kPerWave; ++i) {
+        const int c = (wave + i * kWaves) % Plan::kCopies;
+        const int r = c / Plan::kPerRow, j = c % Plan::kPerRow;
+        if constexpr (WORDS == 0) {
+            const uint32_t col = u * kPartCols + j * 256 + 4 * lane;  // f32 values
+            copy16(ss.hi, stack_lds + (r * a.kt + u * kPartCols + j * 256) * 4,
+                   ((r * a.k + col) * 4) | oob_bit(col < static_cast<uint32_t>(a.k)));
+        } else {
+            if (j < 2 * WORDS) {
+                const int word = j >> 1, half = j & 1;
+                const uint32_t col = u * kPartCols + half * 1024 + 16 * lane;
+                copy16(word == 0 ? ss.hi : ss.lo, stack_lds + (word * R + r) * a.kt + u * kPartCols + half * 1024,
+                       (r * a.k + col) | oob_bit(col < static_cast<uint32_t>(a.k)));
+            } else {
+                const uint32_t blk = u * 64 + lane;
+                copy4(ss.scale, stack_lds + WORDS * R * a.kt + (r * (a.kt / kBlock) + u * 64) * 4,
+                      ((r * a.nb + blk) * 4) | oob_bit(blk < static_cast<uint32_t>(a.nb)));
+            }
+        }
+    }
+}
+
+// s_waitcnt vmcnt(Base + e * Step) for a wave-uniform e in [0, E].
+template <int Base, int Step, int E>
+__device__ __forceinline__ void wait_vm_sel(int e) {
+    if constexpr (E > 0) {
+        if (e == E) {
+            wait_vm<Base + E * Step>();
+            return;
+        }
+        wait_vm_sel<Base, Step, E - 1>(e);
+    } else {
+        wait_vm<Base>();
+    }
+}
+
 __host__ __device__ inline size_t ring_lds_offset(int rows, int words, int kt) {
     return ((stack_bytes(rows, words, kt) + 15) & ~size_t(15)) + static_cast<size_t>(kWaves) * kOutPerWave * 8;
 }
 
-template <int R, int WORDS, int MR, int P>
+// PROG: the stack is copied part by part (above); otherwise it is quantized
+// here from f32 x, whole, before the first item.
+template <int R, int WORDS, int MR, int P, bool PROG>
 __global__ __launch_bounds__(kThreads) void gemv_ring_kernel(GemvArgs a) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & 63;
@@ -642,51 +721,99 @@ __global__ __launch_bounds__(kThreads) void gemv_ring_kernel(GemvArgs a) {
         return static_cast<uint32_t>(min(64, a.nb - c.u * 64)) * kBlockBytes;
     };
 
-    // Prologue: stage the stack, put the first P items in flight, barrier once
-    // the stack has landed.  A stack quantized here goes after the first copies
-    // (its x loads are waited for by count, which then covers the copies too, so
-    // the two latencies overlap); a copied stack goes first, so that the
-    // barrier's wait, which leaves the item copies in flight, covers it.
-    Cursor ahead{0, 0};
-    const bool quantize_here = WORDS != 0 && a.x != nullptr;
-    if (!quantize_here) stage_tile<R, WORDS>(a, lds, 0, wave, lane);
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-        copy_item<MR>(ws, item_base(ahead), item_len(ahead), lane, ring_lds + p * MR * kSlotBytes);
-        ahead.next(ub);
-    }
-    if (quantize_here) stage_tile<R, WORDS>(a, lds, 0, wave, lane);
-    staged_barrier<P * MR * kCopiesPerItemRow>();
-
     double acc[MR][R];
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[m][r] = 0.0;
-
+    auto flush_row = [&](const Cursor &c) {
+        if (c.gi < G && c.u == ub - 1) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const double tot = wave_sum(acc[m][r]);
+                    acc[m][r] = 0.0;
+                    if (lane == 0) totals[(c.gi * MR + m) * R + r] = tot;
+                }
+        }
+    };
+    constexpr int kItemOps = MR * kCopiesPerItemRow;
+    Cursor ahead{0, 0};
     Cursor cur{0, 0};
-    for (int t0 = 0; t0 < T; t0 += P) {
+    if constexpr (PROG) {
+        using Plan = PartPlan<R, WORDS>;
+        static_assert((P - 1) * (kItemOps + Plan::kPerWave) < 64, "vmcnt is six bits");
+        StackStream ss;
+        if constexpr (WORDS == 0) {
+            ss.hi = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.x), 0, R * a.k * 4, kBufferDword3);
+            ss.lo = ss.scale = ss.hi;
+        } else {
+            ss.hi = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(a.hi), 0, R * a.k, kBufferDword3);
+            ss.lo = WORDS == 2 ? __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(a.lo), 0, R * a.k,
+                                                                   kBufferDword3)
+                               : ss.hi;
+            ss.scale = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.scale), 0, R * a.nb * 4,
+                                                         kBufferDword3);
+        }
+        const uint32_t stack_lds = lds_address(lds);
+        // Item t's part (t < ub) goes out just before item t's weights.
+        auto issue = [&](int t, uint32_t slot) {
+            if (t < ub) copy_part<R, WORDS>(a, ss, stack_lds, t, wave, lane);
+            copy_item<MR>(ws, item_base(ahead), item_len(ahead), lane, slot);
+            ahead.next(ub);
+        };
+#pragma unroll
+        for (int p = 0; p < P; ++p) issue(p, ring_lds + p * MR * kSlotBytes);
+        // Every wave, with rows or without, takes part in the first pass's
+        // barriers.
+        const int Tp = max(T, ub);
+        for (int t0 = 0; t0 < Tp; t0 += P) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int t = t0 + p;
+                // this item's copies (and its part) have landed; the later
+                // items in flight carry parts while they are below ub
+                wait_vm_sel<(P - 1) * kItemOps, Plan::kPerWave, P - 1>(min(max(ub - 1 - t, 0), P - 1));
+                if (t < ub) {  // every wave's share of part t has landed
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                    workgroup_barrier_acquire_lds();
+                }
+                Window win[MR];
+                read_item<MR>(ring + p * MR * kSlotBytes, ws.lane_part, win);
+                const Item it{gw + static_cast<int64_t>(cur.gi) * stride, 0, cur.u};
+                compute_item<R, WORDS, MR>(a, lds, it, lane, win, acc);
+                wait_lds_reads();  // the slot is read before it is refilled
+                issue(t + P, ring_lds + p * MR * kSlotBytes);
+                flush_row(cur);
+                cur.next(ub);
+            }
+        }
+    } else {
+        // The stack is quantized here from f32 x after the first copies go out
+        // (its x loads are waited for by count, which then covers the copies
+        // too, so the two latencies overlap), then one barrier.
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-            wait_vm<(P - 1) * MR * kCopiesPerItemRow>();  // this item's copies have landed
-            Window win[MR];
-            read_item<MR>(ring + p * MR * kSlotBytes, ws.lane_part, win);
-            const Item it{gw + static_cast<int64_t>(cur.gi) * stride, 0, cur.u};
-            compute_item<R, WORDS, MR>(a, lds, it, lane, win, acc);
-            wait_lds_reads();  // the slot is read before it is refilled
             copy_item<MR>(ws, item_base(ahead), item_len(ahead), lane, ring_lds + p * MR * kSlotBytes);
             ahead.next(ub);
-            if (cur.gi < G && cur.u == ub - 1) {
+        }
+        stage_tile<R, WORDS>(a, lds, 0, wave, lane);
+        staged_barrier<P * kItemOps>();
+        for (int t0 = 0; t0 < T; t0 += P) {
 #pragma unroll
-                for (int m = 0; m < MR; ++m)
-#pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        const double tot = wave_sum(acc[m][r]);
-                        acc[m][r] = 0.0;
-                        if (lane == 0) totals[(cur.gi * MR + m) * R + r] = tot;
-                    }
+            for (int p = 0; p < P; ++p) {
+                wait_vm<(P - 1) * kItemOps>();  // this item's copies have landed
+                Window win[MR];
+                read_item<MR>(ring + p * MR * kSlotBytes, ws.lane_part, win);
+                const Item it{gw + static_cast<int64_t>(cur.gi) * stride, 0, cur.u};
+                compute_item<R, WORDS, MR>(a, lds, it, lane, win, acc);
+                wait_lds_reads();  // the slot is read before it is refilled
+                copy_item<MR>(ws, item_base(ahead), item_len(ahead), lane, ring_lds + p * MR * kSlotBytes);
+                ahead.next(ub);
+                flush_row(cur);
+                cur.next(ub);
             }
-            cur.next(ub);
         }
     }
     wait_vm<0>();  // the dead refills read nothing but still write the ring
@@ -780,11 +907,20 @@ hipError_t run(GemvArgs a, hipStream_t stream) {
         waves = std::max<int64_t>(waves, min_waves);
         const int64_t grid = (waves + kWaves - 1) / kWaves;
         const size_t lds = ((stack + 15) & ~size_t(15)) + static_cast<size_t>(kWaves) * kOutPerWave * 8;
-        const size_t ring_lds = ring_lds_offset(R, WORDS, a.kt) + static_cast<size_t>(kWaves) * P * MR * kSlotBytes;
+        // the ring kernel stages the stack in whole 2048-column parts
+        const int kt_ring = (a.k + kPartCols - 1) / kPartCols * kPartCols;
+        const size_t ring_lds =
+            ring_lds_offset(R, WORDS, kt_ring) + static_cast<size_t>(kWaves) * P * MR * kSlotBytes;
         const bool aligned = (row_bytes % 16) == 0 && (reinterpret_cast<uintptr_t>(a.w) & 15) == 0;
-        if (aligned && ring_lds * 2 <= static_cast<size_t>(dev.lds_per_block))
-            gemv_ring_kernel<R, WORDS, MR, P><<<dim3(static_cast<unsigned>(grid)), kThreads, ring_lds, stream>>>(a);
-        else
+        if (aligned && ring_lds * 2 <= static_cast<size_t>(dev.lds_per_block)) {
+            GemvArgs b = a;
+            b.kt = kt_ring;
+            const dim3 g(static_cast<unsigned>(grid));
+            if (WORDS != 0 && a.x != nullptr)
+                gemv_ring_kernel<R, WORDS, MR, P, false><<<g, kThreads, ring_lds, stream>>>(b);
+            else
+                gemv_ring_kernel<R, WORDS, MR, P, true><<<g, kThreads, ring_lds, stream>>>(b);
+        } else
             gemv_resident_kernel<R, WORDS, MR, P><<<dim3(static_cast<unsigned>(grid)), kThreads, lds, stream>>>(a);
     } else {
         const int64_t grid = (a.num_groups + kWaves - 1) / kWaves;
