@@ -370,20 +370,30 @@ __device__ __forceinline__ void argmax_finish(const GemvArgs &a, float v, int32_
                 bv = wave_v[w];
                 bi = wave_i[w];
             }
-        part[2 * blockIdx.x] = __float_as_uint(bv);
-        part[2 * blockIdx.x + 1] = static_cast<uint32_t>(bi);
-        // release: the partial is visible before the count; acquire: so is every earlier one
-        const uint32_t done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        // The partial goes out as one agent-scope atomic store, which is written
+        // through this XCD's L2 to the device-coherent level, and it has
+        // completed (vmcnt counts stores too) before the count is taken.  A
+        // release/acquire pair on the counter would instead write back and
+        // invalidate the whole L2 in every workgroup; on the 151936-row head
+        // (512 workgroups) that cost 20 us.
+        const uint64_t packed = (static_cast<uint64_t>(static_cast<uint32_t>(bi)) << 32) | __float_as_uint(bv);
+        __hip_atomic_store(reinterpret_cast<uint64_t *>(part) + blockIdx.x, packed, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const uint32_t done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         is_last = done == gridDim.x - 1;
     }
     __syncthreads();
     if (!is_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // Every other workgroup's partial had completed before its count, and all
+    // counts are in: read them at agent scope too (past this XCD's L2).
     v = -__builtin_inff();
     i = INT32_MAX;
     for (uint32_t b = threadIdx.x; b < gridDim.x; b += blockDim.x) {
-        const float pv = __uint_as_float(part[2 * b]);
-        const int32_t pi = static_cast<int32_t>(part[2 * b + 1]);
+        const uint64_t packed = __hip_atomic_load(reinterpret_cast<const uint64_t *>(part) + b, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        const float pv = __uint_as_float(static_cast<uint32_t>(packed));
+        const int32_t pi = static_cast<int32_t>(packed >> 32);
         if (argmax_better(pv, pi, v, i)) {
             v = pv;
             i = pi;

@@ -47,6 +47,11 @@ constexpr int kRowGranules = kRowChunk / 16;               // 17
 constexpr int kActChunk = kChunkBlocks * kBlock;           // 256 activation bytes per row and word
 constexpr int kTileBytes = 16 * kActChunk;                 // one 16-column activation tile
 constexpr int kCopyBytes = 1024;                           // one copy instruction: 64 lanes x 16 B
+constexpr int kColGranules = kActChunk / 16;               // 16-byte granules of one column's chunk
+constexpr int kColsPerCopy = kCopyBytes / kActChunk;       // column slots one copy fills
+constexpr int kTileCopies = kTileBytes / kCopyBytes;       // copies of one tile
+constexpr int kScaleGranules = kChunkBlocks * 4 / 16;      // 16-byte granules of one row's chunk scales
+static_assert(kChunkBlocks % 8 == 0 && kActChunk <= kCopyBytes, "a chunk is 8, 16 or 32 blocks");
 constexpr int kRingBudget = 156 * 1024;  // LDS for the ring (gfx950: 160 KB per workgroup)
 constexpr int kMaxDepth = 12;
 constexpr int kInFlight = 44 * 1024;  // copy bytes kept in flight per workgroup (measured best)
@@ -58,17 +63,20 @@ typedef __attribute__((address_space(3))) uint8_t *lds_ptr_t;
 
 // Sizes of one ring slot and of the ring, per instantiation.
 //   RT: 16-row weight tiles per workgroup; TT: 16-column activation tiles;
-//   GA x GB waves: wave w takes activation tiles of group w % GA and blocks of
-//   group w / GA of every chunk.
-template <int RT, int TT, int WORDS, int GA, int GB>
+//   GR x GA x GB waves: wave w takes the activation tiles of group w % GA, the
+//   weight tiles of group (w / GA) % GR and the blocks of group w / (GA GR) of
+//   every chunk.  Block groups (GB > 1) split K, and their partial sums are
+//   added by a tree at the end; weight and activation groups split the outputs.
+template <int RT, int TT, int WORDS, int GR, int GA, int GB>
 struct Layout {
-    static constexpr int W = GA * GB;                          // waves per workgroup
+    static constexpr int W = GR * GA * GB;                     // waves per workgroup
     static constexpr int kAT = TT / GA;                        // activation tiles per wave
+    static constexpr int kRTW = RT / GR;                       // weight tiles per wave
     static constexpr int kRows = RT * 16;                      // weight rows a workgroup may own
     static constexpr int kActRows = TT * 16 / WORDS;           // activation rows the tiles hold
     static constexpr int kWCopies = (kRows * kRowGranules + 63) / 64;
-    static constexpr int kACopies = TT * 4;                    // 16 columns x 256 B per tile
-    static constexpr int kSCopies = (kActRows * 2 + 63) / 64;  // 8 f32 scales (2 granules) per row
+    static constexpr int kACopies = TT * kTileCopies;          // 16 columns x kActChunk bytes per tile
+    static constexpr int kSCopies = (kActRows * kScaleGranules + 63) / 64;  // kChunkBlocks f32 scales per row
     static constexpr int kCopies = kWCopies + kACopies + kSCopies;
     static constexpr int kPerWave = (kCopies + W - 1) / W;     // copies of the first kCopies % W waves
     static constexpr int kPerWaveLow = kCopies / W;            // copies of the others
@@ -81,9 +89,9 @@ struct Layout {
         std::max(3, std::min({kMaxDepth, kRingBudget / kSlotBytes, 1 + kInFlight / kSlotBytes}));
     static constexpr int kBlocksPerWave = kChunkBlocks / GB;
     static constexpr int kVals = WORDS == 2 ? 2 : 4;           // f64 accumulators per lane and tile pair
-    static constexpr int kAccBytes = RT * kAT * kVals * 64 * 8; // one wave's accumulators
+    static constexpr int kAccBytes = kRTW * kAT * kVals * 64 * 8; // one wave's accumulators
     static constexpr int kLdsBytes = std::max(kDepth * kSlotBytes, (W / 2) * kAccBytes);
-    static_assert(TT % GA == 0 && kChunkBlocks % GB == 0 && (GB & (GB - 1)) == 0, "wave split");
+    static_assert(TT % GA == 0 && RT % GR == 0 && kChunkBlocks % GB == 0 && (GB & (GB - 1)) == 0, "wave split");
     static_assert(W <= 16, "at most 1024 threads");
     static_assert(kRingBudget / kSlotBytes >= 3, "the ring needs at least three slots");
     static_assert(kPerWave * (kDepth - 2) <= 63, "outstanding copies exceed the vmcnt range");
@@ -151,9 +159,9 @@ __device__ __forceinline__ int act_slot(int m) {
 //   [kSOff, ...)    activation scales, [row][8] f32
 // The result is this lane's offset for chunk 0 (bit 31 set where the lane reads
 // nothing); chunk c adds c * 272, c * 256 or c * 32 to it.
-template <int RT, int TT, int WORDS, int GA, int GB>
+template <int RT, int TT, int WORDS, int GR, int GA, int GB>
 __device__ __forceinline__ uint32_t plan_copy(const MmaArgs &a, int i, int lane, uint32_t r0, int rcount) {
-    using L = Layout<RT, TT, WORDS, GA, GB>;
+    using L = Layout<RT, TT, WORDS, GR, GA, GB>;
     if (i < L::kWCopies) {
         const int g = i * 64 + lane;
         const int row = g / kRowGranules;
@@ -162,16 +170,16 @@ __device__ __forceinline__ uint32_t plan_copy(const MmaArgs &a, int i, int lane,
     }
     if (i < L::kWCopies + L::kACopies) {
         const int ia = i - L::kWCopies;
-        const int t = ia >> 2;
-        const int s = ((ia & 3) << 2) + (lane >> 4);  // column slot
-        const int g = (lane & 15) ^ s;                // granule of the row's 256 chunk bytes
+        const int t = ia / kTileCopies;
+        const int s = (ia % kTileCopies) * kColsPerCopy + lane / kColGranules;  // column slot
+        const int g = (lane % kColGranules) ^ s;  // granule of the row's chunk bytes
         const int row = WORDS == 2 ? t * 8 + (s & 7) : t * 16 + s;
         return (static_cast<uint32_t>(row) * a.k + 16 * g) | oob_bit(row < a.rows);
     }
     if (i < L::kCopies) {
         const int g = (i - L::kWCopies - L::kACopies) * 64 + lane;
-        const int row = g >> 1;
-        return (static_cast<uint32_t>(row) * a.nb * 4 + 16 * (g & 1)) | oob_bit(row < a.rows);
+        const int row = g / kScaleGranules;
+        return (static_cast<uint32_t>(row) * a.nb * 4 + 16 * (g % kScaleGranules)) | oob_bit(row < a.rows);
     }
     return kOob;
 }
@@ -180,11 +188,11 @@ __device__ __forceinline__ uint32_t plan_copy(const MmaArgs &a, int i, int lane,
 // wave i % W, so a wave issues kPerWave or kPerWaveLow copies per chunk, the
 // same number for every chunk (chunks past the end read nothing), and its
 // vmcnt waits are exact.
-template <int RT, int TT, int WORDS, int GA, int GB>
+template <int RT, int TT, int WORDS, int GR, int GA, int GB>
 __device__ __forceinline__ void issue_chunk(const Rsrcs &rs,
-                                            const uint32_t (&base)[Layout<RT, TT, WORDS, GA, GB>::kPerWave],
+                                            const uint32_t (&base)[Layout<RT, TT, WORDS, GR, GA, GB>::kPerWave],
                                             uint32_t slot, int c, int nchunks, int wave) {
-    using L = Layout<RT, TT, WORDS, GA, GB>;
+    using L = Layout<RT, TT, WORDS, GR, GA, GB>;
     constexpr int W = L::W;
     const uint32_t chunk_oob = c < nchunks ? 0u : kOob;
 #pragma unroll
@@ -195,7 +203,8 @@ __device__ __forceinline__ void issue_chunk(const Rsrcs &rs,
         } else if (i < L::kWCopies) {
             copy16(rs.w, slot + i * kCopyBytes, (base[u] + c * kRowChunk) | chunk_oob);
         } else if (i < L::kWCopies + L::kACopies) {
-            const bool lo = WORDS == 2 && ((i - L::kWCopies) & 2);
+            // slots 0..7 hold hi rows, 8..15 lo rows; a copy fills kColsPerCopy of them
+            const bool lo = WORDS == 2 && ((i - L::kWCopies) % kTileCopies) * kColsPerCopy >= 8;
             copy16(lo ? rs.lo : rs.hi, slot + i * kCopyBytes, (base[u] + c * kActChunk) | chunk_oob);
         } else {
             copy16(rs.s, slot + i * kCopyBytes, (base[u] + c * (kChunkBlocks * 4)) | chunk_oob);
@@ -206,32 +215,32 @@ __device__ __forceinline__ void issue_chunk(const Rsrcs &rs,
 // Lane-constant LDS offsets (relative to a slot) of one block's operands.
 struct BlockOffsets {
     uint32_t a;    // activation operand of the wave's first tile (its tile t: + t * kTileBytes)
-    uint32_t b;    // dword-aligned start of the weight operand of row tile 0 (+ rt * 16 * 272)
+    uint32_t b;    // dword-aligned start of the weight operand of the wave's first row tile (+ rt * 16 * 272)
     uint32_t d;    // the weight row's block scale (+ rt * 16 * 272)
     uint32_t s;    // activation scale of the lane's first result column, the wave's first tile
     uint32_t sel;  // v_perm selector realigning the weight operand (uniform)
 };
 
-template <int RT, int TT, int WORDS, int GA, int GB>
-__device__ __forceinline__ BlockOffsets block_offsets(int j, int t0, int lane) {
-    using L = Layout<RT, TT, WORDS, GA, GB>;
+template <int RT, int TT, int WORDS, int GR, int GA, int GB>
+__device__ __forceinline__ BlockOffsets block_offsets(int j, int t0, int r0t, int lane) {
+    using L = Layout<RT, TT, WORDS, GR, GA, GB>;
     const int q = lane >> 4, c16 = lane & 15;
     const int as = act_slot<WORDS>(c16);
     const int boff = j * kBlockBytes + 2 + 8 * q;  // first quant byte of the lane's weight operand
     BlockOffsets o;
     o.a = L::kAOff + t0 * kTileBytes + as * kActChunk + ((((j << 1) + (q >> 1)) ^ as) << 4) + ((q & 1) << 3);
-    o.b = c16 * kRowChunk + (boff & ~3);
-    o.d = c16 * kRowChunk + j * kBlockBytes;
+    o.b = (r0t * 16 + c16) * kRowChunk + (boff & ~3);
+    o.d = (r0t * 16 + c16) * kRowChunk + j * kBlockBytes;
     o.s = L::kSOff + (t0 * (16 / WORDS) + (WORDS == 2 ? 2 * q : 4 * q)) * (kChunkBlocks * 4) + 4 * j;
     o.sel = (boff & 2) ? 0x05040302u : 0x03020100u;
     return o;
 }
 
 // The math of one block of the slot for this wave.
-template <int RT, int TT, int WORDS, int GA, int GB>
+template <int RT, int TT, int WORDS, int GR, int GA, int GB>
 __device__ __forceinline__ void compute_block(const uint8_t *slot, const BlockOffsets &o,
-                                              double (&acc)[RT][Layout<RT, TT, WORDS, GA, GB>::kAT][Layout<RT, TT, WORDS, GA, GB>::kVals]) {
-    using L = Layout<RT, TT, WORDS, GA, GB>;
+                                              double (&acc)[Layout<RT, TT, WORDS, GR, GA, GB>::kRTW][Layout<RT, TT, WORDS, GR, GA, GB>::kAT][Layout<RT, TT, WORDS, GR, GA, GB>::kVals]) {
+    using L = Layout<RT, TT, WORDS, GR, GA, GB>;
     constexpr int AT = L::kAT;
     long aop[AT];
     double s[AT][L::kVals];
@@ -244,7 +253,7 @@ __device__ __forceinline__ void compute_block(const uint8_t *slot, const BlockOf
                 slot + o.s + (t * (16 / WORDS) + v) * (kChunkBlocks * 4)));
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int rt = 0; rt < L::kRTW; ++rt) {
         const uint32_t *pw = reinterpret_cast<const uint32_t *>(slot + o.b + rt * 16 * kRowChunk);
         const uint32_t w0 = pw[0], w1 = pw[1], w2 = pw[2];
         const uint32_t lo32 = __builtin_amdgcn_perm(w1, w0, o.sel);
@@ -269,15 +278,16 @@ __device__ __forceinline__ void compute_block(const uint8_t *slot, const BlockOf
     }
 }
 
-template <int RT, int TT, int WORDS, int GA, int GB>
-__global__ __launch_bounds__(64 * GA * GB, 1) void mma_kernel(MmaArgs a) {
-    using L = Layout<RT, TT, WORDS, GA, GB>;
+template <int RT, int TT, int WORDS, int GR, int GA, int GB>
+__global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_kernel(MmaArgs a) {
+    using L = Layout<RT, TT, WORDS, GR, GA, GB>;
     constexpr int W = L::W;
     constexpr int AT = L::kAT;
     extern __shared__ __align__(16) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int ga = wave % GA, gb = wave / GA;
+    constexpr int RTW = L::kRTW;
+    const int ga = wave % GA, gr = (wave / GA) % GR, gb = wave / (GA * GR);
     const uint32_t r0 = blockIdx.x * static_cast<uint32_t>(a.rows_per_wg);
     const int rcount = static_cast<int>(min(static_cast<uint32_t>(a.rows_per_wg), a.n - r0));
 
@@ -294,15 +304,15 @@ __global__ __launch_bounds__(64 * GA * GB, 1) void mma_kernel(MmaArgs a) {
     uint32_t plan[L::kPerWave];
 #pragma unroll
     for (int u = 0; u < L::kPerWave; ++u)
-        plan[u] = plan_copy<RT, TT, WORDS, GA, GB>(a, wave + W * u, lane, r0, rcount);
+        plan[u] = plan_copy<RT, TT, WORDS, GR, GA, GB>(a, wave + W * u, lane, r0, rcount);
     BlockOffsets offs[L::kBlocksPerWave];
 #pragma unroll
     for (int jj = 0; jj < L::kBlocksPerWave; ++jj)
-        offs[jj] = block_offsets<RT, TT, WORDS, GA, GB>(gb + GB * jj, ga * AT, lane);
+        offs[jj] = block_offsets<RT, TT, WORDS, GR, GA, GB>(gb + GB * jj, ga * AT, gr * RTW, lane);
 
-    double acc[RT][AT][L::kVals];
+    double acc[RTW][AT][L::kVals];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
         for (int t = 0; t < AT; ++t)
 #pragma unroll
@@ -311,7 +321,7 @@ __global__ __launch_bounds__(64 * GA * GB, 1) void mma_kernel(MmaArgs a) {
     // Prologue: chunks 0 .. kDepth-2 in flight.
 #pragma unroll
     for (int c = 0; c < L::kDepth - 1; ++c)
-        issue_chunk<RT, TT, WORDS, GA, GB>(rs, plan, base + c * L::kSlotBytes, c, a.nchunks, wave);
+        issue_chunk<RT, TT, WORDS, GR, GA, GB>(rs, plan, base + c * L::kSlotBytes, c, a.nchunks, wave);
 
     const bool more = wave < L::kCopies % W;  // this wave issues kPerWave copies per chunk, else kPerWaveLow
     int cur = 0;                 // slot of chunk c
@@ -323,28 +333,29 @@ __global__ __launch_bounds__(64 * GA * GB, 1) void mma_kernel(MmaArgs a) {
         else
             wait_copies<L::kPerWaveLow * (L::kDepth - 2)>();
         ring_barrier();  // everyone's have; slot nxt is free
-        issue_chunk<RT, TT, WORDS, GA, GB>(rs, plan, base + nxt * L::kSlotBytes, c + L::kDepth - 1, a.nchunks,
+        issue_chunk<RT, TT, WORDS, GR, GA, GB>(rs, plan, base + nxt * L::kSlotBytes, c + L::kDepth - 1, a.nchunks,
                                            wave);
         const uint8_t *slot = smem + cur * L::kSlotBytes;
 #pragma unroll
-        for (int jj = 0; jj < L::kBlocksPerWave; ++jj) compute_block<RT, TT, WORDS, GA, GB>(slot, offs[jj], acc);
+        for (int jj = 0; jj < L::kBlocksPerWave; ++jj) compute_block<RT, TT, WORDS, GR, GA, GB>(slot, offs[jj], acc);
         cur = cur + 1 == L::kDepth ? 0 : cur + 1;
         nxt = nxt + 1 == L::kDepth ? 0 : nxt + 1;
     }
     wait_copies<0>();  // the trailing copies read nothing but may still write the ring
     ring_barrier();
 
-    // Pairwise tree over the block groups of each activation group: at each
-    // level the upper half parks its accumulators in LDS and the lower half
-    // adds them (fixed order).
+    // Pairwise tree over the block groups of each (weight, activation) group:
+    // at each level the upper half parks its accumulators in LDS and the lower
+    // half adds them (fixed order).
     double *red = reinterpret_cast<double *>(smem);
-    constexpr int kAccVals = RT * AT * L::kVals;
+    constexpr int kAccVals = RTW * AT * L::kVals;
+    const int grp = ga + GA * gr;
 #pragma unroll
     for (int half = GB / 2; half >= 1; half >>= 1) {
         if (gb >= half && gb < 2 * half) {
-            double *dst = red + (ga + GA * (gb - half)) * kAccVals * 64;
+            double *dst = red + (grp + GA * GR * (gb - half)) * kAccVals * 64;
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+            for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
                 for (int t = 0; t < AT; ++t)
 #pragma unroll
@@ -352,9 +363,9 @@ __global__ __launch_bounds__(64 * GA * GB, 1) void mma_kernel(MmaArgs a) {
         }
         ring_barrier();
         if (gb < half) {
-            const double *src = red + (ga + GA * gb) * kAccVals * 64;
+            const double *src = red + (grp + GA * GR * gb) * kAccVals * 64;
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+            for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
                 for (int t = 0; t < AT; ++t)
 #pragma unroll
@@ -366,12 +377,12 @@ __global__ __launch_bounds__(64 * GA * GB, 1) void mma_kernel(MmaArgs a) {
     // [rt][tile][v][lane] and let every wave write a share of the outputs.
     if (gb == 0) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
             for (int t = 0; t < AT; ++t)
 #pragma unroll
                 for (int v = 0; v < L::kVals; ++v)
-                    red[((rt * TT + ga * AT + t) * L::kVals + v) * 64 + lane] = acc[rt][t][v];
+                    red[(((gr * RTW + rt) * TT + ga * AT + t) * L::kVals + v) * 64 + lane] = acc[rt][t][v];
     }
     ring_barrier();
 
@@ -395,25 +406,43 @@ __global__ __launch_bounds__(64 * GA * GB, 1) void mma_kernel(MmaArgs a) {
     }
 }
 
-template <int RT, int TT, int WORDS, int GA, int GB>
+template <int RT, int TT, int WORDS, int GR, int GA, int GB>
 hipError_t run(const MmaArgs &a, hipStream_t stream) {
-    using L = Layout<RT, TT, WORDS, GA, GB>;
+    using L = Layout<RT, TT, WORDS, GR, GA, GB>;
     if (L::kLdsBytes > device_info().lds_per_block) return hipErrorInvalidConfiguration;
     const uint32_t grid = (a.n + a.rows_per_wg - 1) / a.rows_per_wg;
-    hipLaunchKernelGGL((mma_kernel<RT, TT, WORDS, GA, GB>), dim3(grid), dim3(64 * L::W), L::kLdsBytes, stream, a);
+    hipLaunchKernelGGL((mma_kernel<RT, TT, WORDS, GR, GA, GB>), dim3(grid), dim3(64 * L::W), L::kLdsBytes, stream, a);
     return hipGetLastError();
 }
 
-// Wave split per activation-tile count (measured): one tile, eight block
-// groups; two tiles, one per wave, four block groups; four tiles, two per
-// wave, eight block groups; eight tiles, two per wave, four block groups.
+// Wave split per (weight tiles, activation tiles), measured: one activation
+// tile and four weight tiles, two weight groups and four block groups; two
+// activation tiles and one weight tile, sixteen waves (eight block groups);
+// otherwise one weight group and, by activation tiles: one tile, eight block
+// groups; two, one tile a wave and four block groups; four, two tiles a wave
+// and eight block groups; eight, two tiles a wave and four block groups.
+// Splitting the output tiles wider than this (fewer block groups, less
+// operand reuse per wave) measured slower.
+struct Split {
+    int gr, ga, gb;
+};
+constexpr Split wave_split(int rt, int tt) {
+    if (rt == 4 && tt == 1) return Split{2, 1, 4};
+    if (rt == 1 && tt == 2) return Split{1, 2, 8};
+    return Split{1, tt <= 4 ? (tt == 1 ? 1 : 2) : 4, tt == 1 ? 8 : tt == 4 ? 8 : 4};
+}
+
+template <int WORDS, int TT, int RT>
+hipError_t run_split(const MmaArgs &a, hipStream_t s) {
+    constexpr Split sp = wave_split(RT, TT);
+    return run<RT, TT, WORDS, sp.gr, sp.ga, sp.gb>(a, s);
+}
+
 template <int WORDS, int TT>
 hipError_t by_rt(int rt, const MmaArgs &a, hipStream_t s) {
-    constexpr int GA = TT <= 4 ? (TT == 1 ? 1 : 2) : 4;
-    constexpr int GB = TT == 1 ? 8 : TT == 4 ? 8 : 4;
-    if (rt == 1) return run<1, TT, WORDS, GA, GB>(a, s);
-    if (rt == 2) return run<2, TT, WORDS, GA, GB>(a, s);
-    return run<4, TT, WORDS, GA, GB>(a, s);
+    if (rt == 1) return run_split<WORDS, TT, 1>(a, s);
+    if (rt == 2) return run_split<WORDS, TT, 2>(a, s);
+    return run_split<WORDS, TT, 4>(a, s);
 }
 
 // Activation tiles a stack needs.
