@@ -753,7 +753,7 @@ __global__ __launch_bounds__(kThreads) void gemv_ring_kernel(GemvArgs a) {
     Cursor cur{0, 0};
     if constexpr (PROG) {
         using Plan = PartPlan<R, WORDS>;
-        static_assert((P - 1) * (kItemOps + Plan::kPerWave) < 64, "vmcnt is six bits");
+        static_assert(P * (kItemOps + Plan::kPerWave) < 64, "in-flight copies exceed the vmcnt range");
         StackStream ss;
         if constexpr (WORDS == 0) {
             ss.hi = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.x), 0, R * a.k * 4, kBufferDword3);

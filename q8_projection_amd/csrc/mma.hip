@@ -50,7 +50,6 @@ constexpr int kCopyBytes = 1024;                           // one copy instructi
 constexpr int kColGranules = kActChunk / 16;               // 16-byte granules of one column's chunk
 constexpr int kColsPerCopy = kCopyBytes / kActChunk;       // column slots one copy fills
 constexpr int kTileCopies = kTileBytes / kCopyBytes;       // copies of one tile
-constexpr int kScaleGranules = kChunkBlocks * 4 / 16;      // 16-byte granules of one row's chunk scales
 static_assert(kChunkBlocks % 8 == 0 && kActChunk <= kCopyBytes, "a chunk is 8, 16 or 32 blocks");
 constexpr int kRingBudget = 156 * 1024;  // LDS for the ring (gfx950: 160 KB per workgroup)
 constexpr int kMaxDepth = 12;
@@ -76,11 +75,11 @@ struct Layout {
     static constexpr int kActRows = TT * 16 / WORDS;           // activation rows the tiles hold
     static constexpr int kWCopies = (kRows * kRowGranules + 63) / 64;
     static constexpr int kACopies = TT * kTileCopies;          // 16 columns x kActChunk bytes per tile
-    static constexpr int kSCopies = (kActRows * kScaleGranules + 63) / 64;  // kChunkBlocks f32 scales per row
+    static constexpr int kSCopies = kActRows * kChunkBlocks / 64;  // 4-byte copies of the scales, [block][row]
     static constexpr int kCopies = kWCopies + kACopies + kSCopies;
     static constexpr int kPerWave = (kCopies + W - 1) / W;     // copies of the first kCopies % W waves
     static constexpr int kPerWaveLow = kCopies / W;            // copies of the others
-    static constexpr int kSlotBytes = kCopies * kCopyBytes;
+    static constexpr int kSlotBytes = (kWCopies + kACopies) * kCopyBytes + kSCopies * 256;
     static constexpr int kAOff = kWCopies * kCopyBytes;
     static constexpr int kSOff = kAOff + kACopies * kCopyBytes;
     // enough slots for about kInFlight bytes of copies ahead of the math (deeper
@@ -94,8 +93,11 @@ struct Layout {
     static_assert(TT % GA == 0 && RT % GR == 0 && kChunkBlocks % GB == 0 && (GB & (GB - 1)) == 0, "wave split");
     static_assert(W <= 16, "at most 1024 threads");
     static_assert(kRingBudget / kSlotBytes >= 3, "the ring needs at least three slots");
-    static_assert(kPerWave * (kDepth - 2) <= 63, "outstanding copies exceed the vmcnt range");
+    // a wave never has more vector-memory operations in flight than vmcnt can
+    // count (six bits)
+    static_assert(kPerWave * (kDepth - 1) <= 63, "outstanding copies exceed the vmcnt range");
     static_assert(RT * TT * kVals * 64 * 8 <= kLdsBytes, "room for the totals");
+    static_assert(kActRows * kChunkBlocks % 64 == 0, "whole scale copies");
 };
 
 struct MmaArgs {
@@ -121,9 +123,13 @@ struct Rsrcs {
 };
 
 // One direct-to-LDS copy: lane i's 16 bytes at buffer offset `off` land at LDS
-// address lds + 16 i.  An offset with bit 31 set reads zeros and touches no memory.
+// address lds + 16 i (copy4: 4 bytes at lds + 4 i).  An offset with bit 31 set
+// reads zeros and touches no memory.
 __device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t off) {
     asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t off) {
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds) : "memory");
 }
 
 template <int N>
@@ -156,9 +162,10 @@ __device__ __forceinline__ int act_slot(int m) {
 //   [0, kAOff)      weight rows, row-major, 272 bytes each (17 granules)
 //   [kAOff, kSOff)  activation tiles: 16 column slots x 256 bytes, the 16-byte
 //                   granules of slot s XOR-permuted by s
-//   [kSOff, ...)    activation scales, [row][8] f32
+//   [kSOff, ...)    activation scales, [block][row] f32 (copied 4 bytes a lane,
+//                   so that a lane's 4 or 2 rows of one block are adjacent)
 // The result is this lane's offset for chunk 0 (bit 31 set where the lane reads
-// nothing); chunk c adds c * 272, c * 256 or c * 32 to it.
+// nothing); chunk c adds c * kRowChunk, c * kActChunk or c * kChunkBlocks * 4 to it.
 template <int RT, int TT, int WORDS, int GR, int GA, int GB>
 __device__ __forceinline__ uint32_t plan_copy(const MmaArgs &a, int i, int lane, uint32_t r0, int rcount) {
     using L = Layout<RT, TT, WORDS, GR, GA, GB>;
@@ -177,9 +184,9 @@ __device__ __forceinline__ uint32_t plan_copy(const MmaArgs &a, int i, int lane,
         return (static_cast<uint32_t>(row) * a.k + 16 * g) | oob_bit(row < a.rows);
     }
     if (i < L::kCopies) {
-        const int g = (i - L::kWCopies - L::kACopies) * 64 + lane;
-        const int row = g / kScaleGranules;
-        return (static_cast<uint32_t>(row) * a.nb * 4 + 16 * (g % kScaleGranules)) | oob_bit(row < a.rows);
+        const int f = (i - L::kWCopies - L::kACopies) * 64 + lane;  // [block][row] position
+        const int j = f / L::kActRows, row = f % L::kActRows;
+        return (static_cast<uint32_t>(row) * a.nb * 4 + 4 * j) | oob_bit(row < a.rows);
     }
     return kOob;
 }
@@ -207,7 +214,8 @@ __device__ __forceinline__ void issue_chunk(const Rsrcs &rs,
             const bool lo = WORDS == 2 && ((i - L::kWCopies) % kTileCopies) * kColsPerCopy >= 8;
             copy16(lo ? rs.lo : rs.hi, slot + i * kCopyBytes, (base[u] + c * kActChunk) | chunk_oob);
         } else {
-            copy16(rs.s, slot + i * kCopyBytes, (base[u] + c * (kChunkBlocks * 4)) | chunk_oob);
+            copy4(rs.s, slot + L::kSOff + (i - L::kWCopies - L::kACopies) * 256,
+                  (base[u] + c * (kChunkBlocks * 4)) | chunk_oob);
         }
     }
 }
@@ -217,7 +225,7 @@ struct BlockOffsets {
     uint32_t a;    // activation operand of the wave's first tile (its tile t: + t * kTileBytes)
     uint32_t b;    // dword-aligned start of the weight operand of the wave's first row tile (+ rt * 16 * 272)
     uint32_t d;    // the weight row's block scale (+ rt * 16 * 272)
-    uint32_t s;    // activation scale of the lane's first result column, the wave's first tile
+    uint32_t s;    // activation scales of the lane's result columns (4 or 2 adjacent), the wave's first tile
     uint32_t sel;  // v_perm selector realigning the weight operand (uniform)
 };
 
@@ -231,7 +239,7 @@ __device__ __forceinline__ BlockOffsets block_offsets(int j, int t0, int r0t, in
     o.a = L::kAOff + t0 * kTileBytes + as * kActChunk + ((((j << 1) + (q >> 1)) ^ as) << 4) + ((q & 1) << 3);
     o.b = (r0t * 16 + c16) * kRowChunk + (boff & ~3);
     o.d = (r0t * 16 + c16) * kRowChunk + j * kBlockBytes;
-    o.s = L::kSOff + (t0 * (16 / WORDS) + (WORDS == 2 ? 2 * q : 4 * q)) * (kChunkBlocks * 4) + 4 * j;
+    o.s = L::kSOff + (j * L::kActRows + t0 * (16 / WORDS) + (WORDS == 2 ? 2 * q : 4 * q)) * 4;
     o.sel = (boff & 2) ? 0x05040302u : 0x03020100u;
     return o;
 }
@@ -247,10 +255,18 @@ __device__ __forceinline__ void compute_block(const uint8_t *slot, const BlockOf
 #pragma unroll
     for (int t = 0; t < AT; ++t) {
         aop[t] = *reinterpret_cast<const long *>(slot + o.a + t * kTileBytes);
-#pragma unroll
-        for (int v = 0; v < L::kVals; ++v)
-            s[t][v] = static_cast<double>(*reinterpret_cast<const float *>(
-                slot + o.s + (t * (16 / WORDS) + v) * (kChunkBlocks * 4)));
+        const float *ps = reinterpret_cast<const float *>(slot + o.s + t * (16 / WORDS) * 4);
+        if constexpr (WORDS == 2) {
+            const float2 sv = *reinterpret_cast<const float2 *>(ps);
+            s[t][0] = static_cast<double>(sv.x);
+            s[t][1] = static_cast<double>(sv.y);
+        } else {
+            const float4 sv = *reinterpret_cast<const float4 *>(ps);
+            s[t][0] = static_cast<double>(sv.x);
+            s[t][1] = static_cast<double>(sv.y);
+            s[t][2] = static_cast<double>(sv.z);
+            s[t][3] = static_cast<double>(sv.w);
+        }
     }
 #pragma unroll
     for (int rt = 0; rt < L::kRTW; ++rt) {
@@ -415,19 +431,21 @@ hipError_t run(const MmaArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Wave split per (weight tiles, activation tiles), measured: one activation
-// tile and four weight tiles, two weight groups and four block groups; two
-// activation tiles and one weight tile, sixteen waves (eight block groups);
-// otherwise one weight group and, by activation tiles: one tile, eight block
-// groups; two, one tile a wave and four block groups; four, two tiles a wave
-// and eight block groups; eight, two tiles a wave and four block groups.
-// Splitting the output tiles wider than this (fewer block groups, less
+// Wave split per (weight tiles, activation tiles), measured.  One activation
+// tile and four weight tiles: two weight groups and four block groups.  Two
+// activation tiles and one weight tile: sixteen waves (eight block groups).
+// Eight activation tiles and four weight tiles: four tiles a wave and eight
+// block groups.  Otherwise one weight group and, by activation tiles: one tile,
+// eight block groups; two, one tile a wave and four block groups; four, two
+// tiles a wave and eight block groups; eight, two tiles a wave and four block
+// groups.  Splitting the output tiles wider than this (fewer block groups, less
 // operand reuse per wave) measured slower.
 struct Split {
     int gr, ga, gb;
 };
 constexpr Split wave_split(int rt, int tt) {
     if (rt == 4 && tt == 1) return Split{2, 1, 4};
+    if (rt == 4 && tt == 8) return Split{1, 2, 8};
     if (rt == 1 && tt == 2) return Split{1, 2, 8};
     return Split{1, tt <= 4 ? (tt == 1 ? 1 : 2) : 4, tt == 1 ? 8 : tt == 4 ? 8 : 4};
 }

@@ -435,3 +435,27 @@ def test_host_mapped_weights_same_bits():
     assert st == 0
     torch.cuda.synchronize()
     assert torch.equal(y_dev, y_host)
+
+
+# Every instantiation class of the MFMA kernel: a workgroup owns up to 16, 32 or
+# 64 weight rows (n over the chip's 256 CUs: 2000, 6000, 9000) and the stack
+# fills 1, 2, 4 or 8 activation tiles (16 columns each; two-word rows take two).
+_MMA_CASES = [(n, rows, mode) for n in (2000, 6000, 9000)
+              for rows, mode in ((5, "i8"), (24, "i8"), (64, "i8"),
+                                 (5, "i8x2"), (12, "i8x2"), (24, "i8x2"), (64, "i8x2"))]
+
+
+@pytest.mark.parametrize("n,rows,mode", _MMA_CASES)
+def test_mma_instantiations(n, rows, mode):
+    k = 1024
+    say("mma instantiation", n, k, rows, mode)
+    w = synth.weights(n, k, seed=600 + n % 97)
+    x = synth.activations(rows, k, seed=601 + rows)
+    blocks = oracle.quantize_weights(w)
+    wd = to_dev(blocks)
+    hi, lo, sc = q8.quantize_act(mode, to_dev(x))
+    y = q8.matmul_rows(mode, wd, n, k, hi=hi, lo=lo, scale=sc)
+    torch.cuda.synchronize()
+    ohi, olo, osc = oracle.quantize_act(mode, x)
+    r, a = oracle.project(mode, blocks, n, k, rows, hi=ohi, lo=olo, scale=osc)
+    gate(y.cpu().numpy(), r, a, f"mma {n}x{k} rows={rows} {mode}")
