@@ -54,6 +54,15 @@ def step_calls():
             by_name["lm_head"]]
 
 
+def other_calls():
+    """The remaining configurations, timed per call outside the step: the tiny
+    matvec (latency), the attention projection with its residual, and the
+    rows=1 FFN shapes in all three activation modes."""
+    from synth import workloads as wl
+    by_name = {c.name: c for c in wl.all_calls()}
+    return [by_name[n] for n in ("tiny", "attn", "up_f32", "up_i8", "up_i8x2", "down_f32", "down_i8", "down_i8x2")]
+
+
 def kernel_hash(sources) -> str:
     """First 16 hex digits of the SHA-256 over the named kernel sources, in order."""
     h = hashlib.sha256()
@@ -117,13 +126,15 @@ class Prepared:
 
     def quantize(self):
         import q8_projection_amd as q8
-        if not self.inside:
+        if not self.inside and self.call.mode != "f32":
             q8.quantize_act(self.call.mode, self.x, hi=self.hi, lo=self.lo, scale=self.sc)
 
     def project(self, copy):
         import q8_projection_amd as q8
         c = self.call
-        if self.inside:
+        if c.mode == "f32":
+            q8.matmul_rows(c.mode, self.w[copy], c.n, c.k, x=self.x, residual=self.res, out=self.y)
+        elif self.inside:
             q8.matmul_rows(c.mode, self.w[copy], c.n, c.k, x=self.x,
                            residual=self.res, out=self.y)
         elif c.rows == 1:
@@ -161,6 +172,29 @@ def sweep(spec: str, dev):
                           "GBps": round(call.weight_bytes / t / 1e9, 1),
                           "pct_hbm_peak": round(call.weight_bytes / t / 1e9 / HBM_PEAK_GBPS * 100, 1),
                           "rows_GFLOPs": round(call.flops / t / 1e9, 1)}), flush=True)
+
+
+def time_calls(prepared, reps):
+    """Per call: projection (and separate quantization) time from graphs of
+    `reps` back-to-back launches on rotating weight copies."""
+    out = {}
+    for p in prepared:
+        p.quantize()
+        separate = not p.inside and p.call.mode != "f32"
+        gq = capture(lambda p=p: p.quantize(), reps) if separate else None
+        gp = capture(lambda p=p: [p.project(i % p.copies) for i in range(reps)])
+        tq = 0.0 if gq is None else time_graph(gq, 5) / reps
+        tp = time_graph(gp, 5) / reps
+        out[p.call.name] = {"rows": p.call.rows, "n": p.call.n, "k": p.call.k, "mode": p.call.mode,
+                            "weight_bytes": p.call.weight_bytes,
+                            "project_us": round(tp * 1e6, 3),
+                            "quantize_us": round(tq * 1e6, 3) if separate else None,
+                            "quantize_inside": p.inside,
+                            "GBps": round(p.call.weight_bytes / tp / 1e9, 1),
+                            "pct_hbm_peak": round(p.call.weight_bytes / tp / 1e9 / HBM_PEAK_GBPS * 100, 1),
+                            "rows_GFLOPs": round(p.call.flops / tp / 1e9, 1),
+                            "hbm_bytes_counted": stored_traffic(p.call.name)}
+    return out
 
 
 def time_head_argmax(p, reps):
@@ -352,24 +386,18 @@ def main(argv=None):
     step_bytes = sum(c.weight_bytes for c in calls)
 
     # per-call kernel times: a graph of back-to-back launches cycling the copies
-    per_call = {}
     reps = 20
-    for p in prepared:
-        p.quantize()
-        gq = None if p.inside else capture(lambda p=p: p.quantize(), reps)
-        gp = capture(lambda p=p: [p.project(i % p.copies) for i in range(reps)])
-        tq = 0.0 if gq is None else time_graph(gq, 5) / reps
-        tp = time_graph(gp, 5) / reps
-        per_call[p.call.name] = {"rows": p.call.rows, "n": p.call.n, "k": p.call.k, "mode": p.call.mode,
-                                 "weight_bytes": p.call.weight_bytes,
-                                 "project_us": round(tp * 1e6, 3),
-                                 "quantize_us": None if p.inside else round(tq * 1e6, 3),
-                                 "quantize_inside": p.inside,
-                                 "GBps": round(p.call.weight_bytes / tp / 1e9, 1),
-                                 "pct_hbm_peak": round(p.call.weight_bytes / tp / 1e9 / HBM_PEAK_GBPS * 100, 1),
-                                 "rows_GFLOPs": round(p.call.flops / tp / 1e9, 1),
-                                 "hbm_bytes_counted": stored_traffic(p.call.name)}
+    per_call = time_calls(prepared, reps)
     head_argmax = time_head_argmax(next(p for p in prepared if p.call.name == "lm_head"), reps)
+    weight_copies = {p.call.name: p.copies for p in prepared}
+    del graphs, ref, prepared  # free the step's buffers before the other calls
+    torch.cuda.empty_cache()
+    others = [Prepared(c, dev) for c in other_calls()]
+    other = time_calls(others, reps)
+    for d in other.values():
+        del d["hbm_bytes_counted"]
+    del others
+    torch.cuda.empty_cache()
     by_rows = {}
     for name, d in per_call.items():
         key = str(d["rows"])
@@ -408,11 +436,12 @@ def main(argv=None):
                                "rows=8 (14336x4096 two-word; 4096x14336 two-word + residual) + prefill rows=64 "
                                "(14336x4096, one-word) + LM head on the last row (151936x2048, one-word)",
                    "weight_bytes_per_step": step_bytes, "graph_replay": True,
-                   "weight_copies": {p.call.name: p.copies for p in prepared}},
+                   "weight_copies": weight_copies},
         "pct_hbm_peak": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBPS * 100, 1),
         "per_rows": per_rows,
         "per_call": per_call,
         "lm_head_argmax": head_argmax,
+        "other_calls": other,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -89,15 +89,26 @@ __device__ __forceinline__ void lds_copy4(const void *src, uint32_t lds) {
     asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
+// f32 stacks in LDS: the eight 16-byte granules of each 32-value block sit in
+// the order j ^ (block & 7).  A lane reads its own block's granules, so lanes
+// of one block apart are 128 bytes apart; in plain order the 16-byte reads of
+// eight neighbouring lanes all fell on the same four banks.  Swizzled, they
+// cover every bank.  The copies place it: a lane picks its source granule.
+__host__ __device__ constexpr int f32_granule(int block, int j) { return j ^ (block & 7); }
+
 // rows x bytes (bytes a multiple of 16) from src (row stride src_stride) to LDS
-// dst (row stride dst_stride), 16 bytes per lane.
+// dst (row stride dst_stride), 16 bytes per lane.  F32_SWIZZLE: the rows are
+// f32 values (bytes a multiple of 128), stored in the order above.
+template <bool F32_SWIZZLE = false>
 __device__ __forceinline__ void dma_rows16(uint8_t *dst, int dst_stride, const uint8_t *src, int64_t src_stride,
                                            int rows, int bytes, int wave, int lane) {
     const int per_row = (bytes + 1023) / 1024;
+    // a copy covers 1 KB = 8 whole blocks, so lane / 8 is the block's index mod 8
+    const int from = F32_SWIZZLE ? (lane & ~7) + f32_granule(lane >> 3, lane & 7) : lane;
     for (int c = wave; c < rows * per_row; c += kWaves) {
         const int r = c / per_row, off = (c - r * per_row) * 1024;
         const uint32_t to = lds_address(dst + r * dst_stride + off);
-        if (off + lane * 16 < bytes) lds_copy16(src + r * src_stride + off + lane * 16, to);
+        if (off + lane * 16 < bytes) lds_copy16(src + r * src_stride + off + from * 16, to);
     }
 }
 
@@ -174,8 +185,8 @@ __device__ __forceinline__ void stage_quant(const GemvArgs &a, uint8_t *lds, int
 template <int R>
 __device__ __forceinline__ void stage_f32(const GemvArgs &a, uint8_t *lds, int ti, int wave, int lane) {
     const int kt0 = ti * a.kt, ktc = min(a.kt, a.k - kt0);
-    dma_rows16(lds, a.kt * 4, reinterpret_cast<const uint8_t *>(a.x + kt0), static_cast<int64_t>(a.k) * 4, R,
-               ktc * 4, wave, lane);
+    dma_rows16<true>(lds, a.kt * 4, reinterpret_cast<const uint8_t *>(a.x + kt0), static_cast<int64_t>(a.k) * 4, R,
+                     ktc * 4, wave, lane);
 }
 
 // ------------------------------------------------------------- weight windows
@@ -285,7 +296,7 @@ __device__ __forceinline__ void compute_f64_item(const GemvArgs &a, const uint8_
         double p = 0.0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float4 xv = px[j];
+            const float4 xv = px[f32_granule(bl, j)];
             const uint32_t qw = q[j];
             p = __builtin_fma(static_cast<double>(static_cast<int8_t>(qw)), static_cast<double>(xv.x), p);
             p = __builtin_fma(static_cast<double>(static_cast<int8_t>(qw >> 8)), static_cast<double>(xv.y), p);
@@ -662,7 +673,9 @@ __device__ __forceinline__ void copy_part(const GemvArgs &a, const StackStream &
         const int c = (wave + i * kWaves) % Plan::kCopies;
         const int r = c / Plan::kPerRow, j = c % Plan::kPerRow;
         if constexpr (WORDS == 0) {
-            const uint32_t col = u * kPartCols + j * 256 + 4 * lane;  // f32 values
+            // f32 values, 8 blocks a copy, in the swizzled granule order
+            const int from = (lane & ~7) + f32_granule(lane >> 3, lane & 7);
+            const uint32_t col = u * kPartCols + j * 256 + 4 * from;
             copy16(ss.hi, stack_lds + (r * a.kt + u * kPartCols + j * 256) * 4,
                    ((r * a.k + col) * 4) | oob_bit(col < static_cast<uint32_t>(a.k)));
         } else {

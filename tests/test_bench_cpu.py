@@ -12,6 +12,15 @@ def test_step_calls_are_the_measured_workloads():
     assert rows == [1, 8, 64]
 
 
+def test_other_calls_cover_every_mode_and_the_small_configs():
+    calls = bench.other_calls()
+    names = [c.name for c in calls]
+    assert "tiny" in names and "attn" in names
+    for shape in ("up", "down"):
+        assert sorted(c.mode for c in calls if c.name.startswith(shape + "_")) == ["f32", "i8", "i8x2"]
+    assert not set(names) & {c.name for c in bench.step_calls()} - {"down_i8x2"}
+
+
 def test_more_than_one_gpu_is_refused():
     assert bench.main(["--gpus", "2"]) == 2
 
