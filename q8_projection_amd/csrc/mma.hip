@@ -56,6 +56,9 @@ constexpr int kMaxDepth = 12;
 constexpr int kInFlight = 44 * 1024;  // copy bytes kept in flight per workgroup (measured best)
 constexpr uint32_t kBufferDword3 = 0x00020000u;
 constexpr uint32_t kOob = 0x80000000u;
+constexpr int kWaveMaxRt = 1;     // single-tile stacks on matrices this short use the wave-private kernel
+constexpr int kWaveWaves = 8;
+constexpr int kWaveDepth = 2;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t *lds_ptr_t;
@@ -422,6 +425,113 @@ __global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_kernel(MmaArgs a) {
     }
 }
 
+// ------------------------------------------------ one tile, wave-private rings
+//
+// A stack of one activation tile (up to 8 two-word or 16 one-word rows) against
+// a 16-row weight tile, for short matrices where a workgroup owns a single tile.
+// The shared-ring kernel above hands every chunk to all its waves through a
+// barrier; with one tile each wave then has a single block of math per chunk,
+// and the chunk's copy issue, its barrier and that block run in series.  Here
+// the W waves split the chunks instead (wave w takes chunks w, w + W, ...):
+// each copies its own chunks (weights, activation tile and scales, laid out as
+// the shared slot is) into a private ring of P slots, waits for them by count
+// and computes all eight blocks, with no barrier until the end.  The waves'
+// partial sums are then added in wave order and each output rounded once.
+template <int WORDS, int W, int P>
+struct WaveLayout {
+    using L = Layout<1, 1, WORDS, 1, 1, 1>;  // one wave issuing every copy of a chunk
+    static constexpr int kVals = L::kVals;
+    static constexpr int kRing = P * L::kSlotBytes;  // one wave's ring
+    static constexpr int kLdsBytes = std::max(W * kRing, W * kVals * 64 * 8);
+    static_assert(P >= 2 && P * L::kCopies <= 63, "outstanding copies exceed the vmcnt range");
+    static_assert(W >= 1 && W <= 16, "at most 1024 threads");
+};
+
+template <int WORDS, int W, int P>
+__global__ __launch_bounds__(64 * W, 1) void mma_wave_kernel(MmaArgs a) {
+    using WL = WaveLayout<WORDS, W, P>;
+    using L = typename WL::L;
+    constexpr int V = WL::kVals;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t r0 = blockIdx.x * 16u;
+    const int rcount = static_cast<int>(min(16u, a.n - r0));
+
+    Rsrcs rs;
+    rs.w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.w), 0, a.w_bytes, kBufferDword3);
+    const uint32_t act_bytes = static_cast<uint32_t>(a.rows) * a.k;
+    rs.hi = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(a.hi), 0, act_bytes, kBufferDword3);
+    rs.lo = WORDS == 2 ? __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(a.lo), 0, act_bytes, kBufferDword3)
+                       : rs.hi;
+    rs.s = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.scale), 0,
+                                             static_cast<uint32_t>(a.rows) * a.nb * 4, kBufferDword3);
+    const uint8_t *ring = smem + wave * WL::kRing;
+    const uint32_t ring_lds =
+        __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((uintptr_t)(lds_ptr_t)smem)) + wave * WL::kRing;
+
+    uint32_t plan[L::kPerWave];
+#pragma unroll
+    for (int u = 0; u < L::kPerWave; ++u) plan[u] = plan_copy<1, 1, WORDS, 1, 1, 1>(a, u, lane, r0, rcount);
+    BlockOffsets offs[kChunkBlocks];
+#pragma unroll
+    for (int j = 0; j < kChunkBlocks; ++j) offs[j] = block_offsets<1, 1, WORDS, 1, 1, 1>(j, 0, 0, lane);
+
+    double acc[1][1][V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[0][0][v] = 0.0;
+
+    // this wave's chunks: wave, wave + W, ...; copies past the last chunk read
+    // nothing, so every step issues the same number and the counts stay exact
+    const int mine = wave < a.nchunks ? (a.nchunks - wave + W - 1) / W : 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+        issue_chunk<1, 1, WORDS, 1, 1, 1>(rs, plan, ring_lds + p * L::kSlotBytes, wave + W * p, a.nchunks, 0);
+    int slot = 0;
+    for (int i = 0; i < mine; ++i) {
+        wait_copies<(P - 1) * L::kCopies>();  // chunk i's copies have landed
+        const uint8_t *s = ring + slot * L::kSlotBytes;
+#pragma unroll
+        for (int j = 0; j < kChunkBlocks; ++j) compute_block<1, 1, WORDS, 1, 1, 1>(s, offs[j], acc);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot is read before it is refilled
+        issue_chunk<1, 1, WORDS, 1, 1, 1>(rs, plan, ring_lds + slot * L::kSlotBytes, wave + W * (i + P), a.nchunks,
+                                          0);
+        slot = slot + 1 == P ? 0 : slot + 1;
+    }
+    wait_copies<0>();  // the trailing copies read nothing but still write the ring
+    ring_barrier();    // every wave is done with its ring
+
+    double *red = reinterpret_cast<double *>(smem);
+#pragma unroll
+    for (int v = 0; v < V; ++v) red[(wave * V + v) * 64 + lane] = acc[0][0][v];
+    ring_barrier();
+    if (wave != 0) return;
+    const double post = WORDS == 2 ? 1.0 / 128.0 : 1.0;
+    const int q = lane >> 4, c16 = lane & 15;
+    if (c16 >= rcount) return;
+    const uint32_t n = r0 + c16;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int ar = WORDS == 2 ? 2 * q + v : 4 * q + v;
+        if (ar >= a.rows) continue;
+        double tot = red[v * 64 + lane];
+        for (int w = 1; w < W; ++w) tot += red[(w * V + v) * 64 + lane];
+        const int64_t o = static_cast<int64_t>(ar) * a.ldy + n;
+        const double res = a.residual ? static_cast<double>(a.residual[o]) : 0.0;
+        a.y[o] = static_cast<float>(tot * post + res);
+    }
+}
+
+template <int WORDS, int W, int P>
+hipError_t run_wave(MmaArgs a, hipStream_t stream) {
+    using WL = WaveLayout<WORDS, W, P>;
+    if (WL::kLdsBytes > device_info().lds_per_block) return hipErrorInvalidConfiguration;
+    a.rows_per_wg = 16;
+    const uint32_t grid = (a.n + 15) / 16;
+    hipLaunchKernelGGL((mma_wave_kernel<WORDS, W, P>), dim3(grid), dim3(64 * W), WL::kLdsBytes, stream, a);
+    return hipGetLastError();
+}
+
 template <int RT, int TT, int WORDS, int GR, int GA, int GB>
 hipError_t run(const MmaArgs &a, hipStream_t stream) {
     using L = Layout<RT, TT, WORDS, GR, GA, GB>;
@@ -511,6 +621,10 @@ hipError_t launch_mma(int mode, const uint8_t *w, int64_t n, int64_t k, int rows
     a.rows = rows;
     a.rows_per_wg = static_cast<int>(per_wg);
     a.nchunks = static_cast<int>(nb / kChunkBlocks);
+    if (at == 1 && rt <= kWaveMaxRt) {
+        if (words == 2) return run_wave<2, kWaveWaves, kWaveDepth>(a, stream);
+        return run_wave<1, kWaveWaves, kWaveDepth>(a, stream);
+    }
     if (words == 2) {
         switch (at) {
             case 1: return by_rt<2, 1>(rt, a, stream);

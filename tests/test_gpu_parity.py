@@ -205,11 +205,16 @@ def test_ragged_shapes(mode, n, k, rows):
 def test_stack_rows_equal_single_rows():
     """A row's result does not depend on the rest of its stack.  f32 mode (the
     GEMV family at every stack height): a stacked row equals that row alone.
-    Integer modes (the MFMA family serves 4..64 rows here, with one summation
-    order per output whatever the stack): a row of an 8-row stack equals the
-    same row in a 4-row and in a 64-row stack.  Rows of a stack are within the
-    gate of the same row projected alone by the GEMV (different summation
-    order)."""
+    Integer modes, on a matrix short enough that a workgroup owns one 16-row
+    weight tile: stacks of one activation tile (up to 8 two-word or 16 one-word
+    rows) run on the wave-private MFMA kernel, taller ones on the shared-ring
+    MFMA kernel.  Block terms are summed in f64 and each output is rounded once
+    to f32, so where two stacks add the terms in different orders their f64
+    totals differ by a few f64 ulps at most and the f32 outputs agree unless a
+    total falls that close to an f32 rounding boundary (none does for this
+    seeded input).  A row of an 8-row stack equals the same row in a 4-row
+    stack, and a row of a 64-row stack the same row in a 24-row and in the
+    8-row stack.  The GEMV on the row alone is within the gate."""
     n, k = 515, 4096
     say("stack vs single rows", n, k)
     w = synth.weights(n, k, seed=501)
@@ -224,18 +229,23 @@ def test_stack_rows_equal_single_rows():
         assert torch.equal(ys[r], singles[r]), ("f32", r)
     for mode in ("i8", "i8x2"):
         hi, lo, sc = q8.quantize_act(mode, to_dev(x64))
-        ys64 = q8.matmul_rows(mode, wd, n, k, hi=hi, lo=lo, scale=sc)
-        ys8 = q8.matmul_rows(mode, wd, n, k, hi=hi[:8], lo=None if lo is None else lo[:8], scale=sc[:8])
+
+        def stack(r0, r1):
+            return q8.matmul_rows(mode, wd, n, k, hi=hi[r0:r1], lo=None if lo is None else lo[r0:r1],
+                                  scale=sc[r0:r1])
+
+        ys64, ys24, ys8 = stack(0, 64), stack(0, 24), stack(0, 8)
         for r0 in range(0, 8, 4):
-            ys4 = q8.matmul_rows(mode, wd, n, k, hi=hi[r0:r0 + 4], lo=None if lo is None else lo[r0:r0 + 4],
-                                 scale=sc[r0:r0 + 4])
+            ys4 = stack(r0, r0 + 4)
             torch.cuda.synchronize()
             assert torch.equal(ys8[r0:r0 + 4], ys4), (mode, r0)
         torch.cuda.synchronize()
+        assert torch.equal(ys64[:24], ys24), mode
         assert torch.equal(ys64[:8], ys8), mode
-        ohi, olo, osc = oracle.quantize_act(mode, x64[:8])
-        r, a = oracle.project(mode, blocks, n, k, 8, hi=ohi, lo=olo, scale=osc)
-        gate(ys8.cpu().numpy(), r, a, f"stack {mode}")
+        ohi, olo, osc = oracle.quantize_act(mode, x64)
+        r, a = oracle.project(mode, blocks, n, k, 64, hi=ohi, lo=olo, scale=osc)
+        gate(ys8.cpu().numpy(), r[:8], a[:8], f"stack of 8 {mode}")
+        gate(ys64.cpu().numpy(), r, a, f"stack of 64 {mode}")
         one = q8.matvec(mode, wd, n, k, hi=hi[3], lo=None if lo is None else lo[3], scale=sc[3])
         torch.cuda.synchronize()
         gate(one.cpu().numpy(), r[3], a[3], f"single {mode}")
@@ -435,6 +445,29 @@ def test_host_mapped_weights_same_bits():
     assert st == 0
     torch.cuda.synchronize()
     assert torch.equal(y_dev, y_host)
+
+
+# The wave-private MFMA kernel (one 16-row weight tile per workgroup, one
+# activation tile): fewer chunks than waves, chunks that do not divide among the
+# waves, a partial last tile, full one-word tiles, and the residual epilogue.
+_WAVE_CASES = [(37, 256, 4, "i8x2", False), (1000, 2304, 7, "i8", True), (4000, 4096, 16, "i8", False),
+               (100, 8192, 8, "i8x2", True), (4096, 1024, 5, "i8x2", True), (4001, 14336, 8, "i8x2", False)]
+
+
+@pytest.mark.parametrize("n,k,rows,mode,with_res", _WAVE_CASES)
+def test_mma_wave_kernel(n, k, rows, mode, with_res):
+    say("mma wave kernel", n, k, rows, mode, with_res)
+    w = synth.weights(n, k, seed=700 + n % 89)
+    x = synth.activations(rows, k, seed=701 + rows)
+    res = synth.normal(702, (rows, n)) if with_res else None
+    blocks = oracle.quantize_weights(w)
+    wd = to_dev(blocks)
+    hi, lo, sc = q8.quantize_act(mode, to_dev(x))
+    y = q8.matmul_rows(mode, wd, n, k, hi=hi, lo=lo, scale=sc, residual=None if res is None else to_dev(res))
+    torch.cuda.synchronize()
+    ohi, olo, osc = oracle.quantize_act(mode, x)
+    r, a = oracle.project(mode, blocks, n, k, rows, hi=ohi, lo=olo, scale=osc, residual=res)
+    gate(y.cpu().numpy(), r, a, f"mma wave {n}x{k} rows={rows} {mode}")
 
 
 # Every instantiation class of the MFMA kernel: a workgroup owns up to 16, 32 or
