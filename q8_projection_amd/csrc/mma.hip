@@ -247,42 +247,70 @@ __device__ __forceinline__ BlockOffsets block_offsets(int j, int t0, int r0t, in
     return o;
 }
 
-// The math of one block of the slot for this wave.
+// One block's operands for this wave, read from the slot: the activation
+// operands and scales of its tiles, the weight window and scale of each of its
+// row tiles.  Every LDS read of a block (or of several) is issued before any
+// of them is used, so their latencies overlap.
 template <int RT, int TT, int WORDS, int GR, int GA, int GB>
-__device__ __forceinline__ void compute_block(const uint8_t *slot, const BlockOffsets &o,
-                                              double (&acc)[Layout<RT, TT, WORDS, GR, GA, GB>::kRTW][Layout<RT, TT, WORDS, GR, GA, GB>::kAT][Layout<RT, TT, WORDS, GR, GA, GB>::kVals]) {
+struct BlockOps {
     using L = Layout<RT, TT, WORDS, GR, GA, GB>;
-    constexpr int AT = L::kAT;
-    long aop[AT];
-    double s[AT][L::kVals];
+    long a[L::kAT];
+    float s[L::kAT][L::kVals];
+    uint32_t w[L::kRTW][3];
+    uint16_t d[L::kRTW];
+};
+
+template <int RT, int TT, int WORDS, int GR, int GA, int GB>
+__device__ __forceinline__ void load_block(const uint8_t *slot, const BlockOffsets &o,
+                                           BlockOps<RT, TT, WORDS, GR, GA, GB> &op) {
+    using L = Layout<RT, TT, WORDS, GR, GA, GB>;
 #pragma unroll
-    for (int t = 0; t < AT; ++t) {
-        aop[t] = *reinterpret_cast<const long *>(slot + o.a + t * kTileBytes);
+    for (int t = 0; t < L::kAT; ++t) {
+        op.a[t] = *reinterpret_cast<const long *>(slot + o.a + t * kTileBytes);
         const float *ps = reinterpret_cast<const float *>(slot + o.s + t * (16 / WORDS) * 4);
         if constexpr (WORDS == 2) {
             const float2 sv = *reinterpret_cast<const float2 *>(ps);
-            s[t][0] = static_cast<double>(sv.x);
-            s[t][1] = static_cast<double>(sv.y);
+            op.s[t][0] = sv.x;
+            op.s[t][1] = sv.y;
         } else {
             const float4 sv = *reinterpret_cast<const float4 *>(ps);
-            s[t][0] = static_cast<double>(sv.x);
-            s[t][1] = static_cast<double>(sv.y);
-            s[t][2] = static_cast<double>(sv.z);
-            s[t][3] = static_cast<double>(sv.w);
+            op.s[t][0] = sv.x;
+            op.s[t][1] = sv.y;
+            op.s[t][2] = sv.z;
+            op.s[t][3] = sv.w;
         }
     }
 #pragma unroll
     for (int rt = 0; rt < L::kRTW; ++rt) {
         const uint32_t *pw = reinterpret_cast<const uint32_t *>(slot + o.b + rt * 16 * kRowChunk);
-        const uint32_t w0 = pw[0], w1 = pw[1], w2 = pw[2];
-        const uint32_t lo32 = __builtin_amdgcn_perm(w1, w0, o.sel);
-        const uint32_t hi32 = __builtin_amdgcn_perm(w2, w1, o.sel);
+        op.w[rt][0] = pw[0];
+        op.w[rt][1] = pw[1];
+        op.w[rt][2] = pw[2];
+        op.d[rt] = *reinterpret_cast<const uint16_t *>(slot + o.d + rt * 16 * kRowChunk);
+    }
+}
+
+// The math of one block for this wave: realign the weight windows, one MFMA
+// per (row tile, activation tile), and each term (d * s) * T into f64.
+template <int RT, int TT, int WORDS, int GR, int GA, int GB>
+__device__ __forceinline__ void math_block(const BlockOps<RT, TT, WORDS, GR, GA, GB> &op, uint32_t sel,
+                                           double (&acc)[Layout<RT, TT, WORDS, GR, GA, GB>::kRTW][Layout<RT, TT, WORDS, GR, GA, GB>::kAT][Layout<RT, TT, WORDS, GR, GA, GB>::kVals]) {
+    using L = Layout<RT, TT, WORDS, GR, GA, GB>;
+    constexpr int AT = L::kAT;
+    double s[AT][L::kVals];
+#pragma unroll
+    for (int t = 0; t < AT; ++t)
+#pragma unroll
+        for (int v = 0; v < L::kVals; ++v) s[t][v] = static_cast<double>(op.s[t][v]);
+#pragma unroll
+    for (int rt = 0; rt < L::kRTW; ++rt) {
+        const uint32_t lo32 = __builtin_amdgcn_perm(op.w[rt][1], op.w[rt][0], sel);
+        const uint32_t hi32 = __builtin_amdgcn_perm(op.w[rt][2], op.w[rt][1], sel);
         const long bop = static_cast<long>((static_cast<uint64_t>(hi32) << 32) | lo32);
-        const uint16_t dbits = *reinterpret_cast<const uint16_t *>(slot + o.d + rt * 16 * kRowChunk);
-        const double d = static_cast<double>(f16_bits_to_float(dbits));
+        const double d = static_cast<double>(f16_bits_to_float(op.d[rt]));
 #pragma unroll
         for (int t = 0; t < AT; ++t) {
-            const v4i sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[t], bop, v4i{0, 0, 0, 0}, 0, 0, 0);
+            const v4i sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(op.a[t], bop, v4i{0, 0, 0, 0}, 0, 0, 0);
             if constexpr (WORDS == 2) {
                 const int t0 = sum[0] * 128 + sum[1];
                 const int t1 = sum[2] * 128 + sum[3];
@@ -295,6 +323,18 @@ __device__ __forceinline__ void compute_block(const uint8_t *slot, const BlockOf
             }
         }
     }
+}
+
+// Blocks offs[0..NB) of a slot, in that order: every operand read first.
+template <int RT, int TT, int WORDS, int GR, int GA, int GB, int NB>
+__device__ __forceinline__ void compute_blocks(const uint8_t *slot, const BlockOffsets (&offs)[NB],
+                                               double (&acc)[Layout<RT, TT, WORDS, GR, GA, GB>::kRTW][Layout<RT, TT, WORDS, GR, GA, GB>::kAT][Layout<RT, TT, WORDS, GR, GA, GB>::kVals]) {
+    BlockOps<RT, TT, WORDS, GR, GA, GB> op[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) load_block<RT, TT, WORDS, GR, GA, GB>(slot, offs[j], op[j]);
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the math: the scheduler would sink them
+#pragma unroll
+    for (int j = 0; j < NB; ++j) math_block<RT, TT, WORDS, GR, GA, GB>(op[j], offs[j].sel, acc);
 }
 
 template <int RT, int TT, int WORDS, int GR, int GA, int GB>
@@ -355,8 +395,7 @@ __global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_kernel(MmaArgs a) {
         issue_chunk<RT, TT, WORDS, GR, GA, GB>(rs, plan, base + nxt * L::kSlotBytes, c + L::kDepth - 1, a.nchunks,
                                            wave);
         const uint8_t *slot = smem + cur * L::kSlotBytes;
-#pragma unroll
-        for (int jj = 0; jj < L::kBlocksPerWave; ++jj) compute_block<RT, TT, WORDS, GR, GA, GB>(slot, offs[jj], acc);
+        compute_blocks<RT, TT, WORDS, GR, GA, GB, L::kBlocksPerWave>(slot, offs, acc);
         cur = cur + 1 == L::kDepth ? 0 : cur + 1;
         nxt = nxt + 1 == L::kDepth ? 0 : nxt + 1;
     }
@@ -491,8 +530,7 @@ __global__ __launch_bounds__(64 * W, 1) void mma_wave_kernel(MmaArgs a) {
     for (int i = 0; i < mine; ++i) {
         wait_copies<(P - 1) * L::kCopies>();  // chunk i's copies have landed
         const uint8_t *s = ring + slot * L::kSlotBytes;
-#pragma unroll
-        for (int j = 0; j < kChunkBlocks; ++j) compute_block<1, 1, WORDS, 1, 1, 1>(s, offs[j], acc);
+        compute_blocks<1, 1, WORDS, 1, 1, 1, kChunkBlocks>(s, offs, acc);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot is read before it is refilled
         issue_chunk<1, 1, WORDS, 1, 1, 1>(rs, plan, ring_lds + slot * L::kSlotBytes, wave + W * (i + P), a.nchunks,
                                           0);
