@@ -447,16 +447,20 @@ def test_host_mapped_weights_same_bits():
     assert torch.equal(y_dev, y_host)
 
 
-# The wave-private MFMA kernel (one 16-row weight tile per workgroup, one
-# activation tile): fewer chunks than waves, chunks that do not divide among the
-# waves, a partial last tile, full one-word tiles, and the residual epilogue.
+# Stacks of one activation tile (up to 8 two-word or 16 one-word rows): on a
+# matrix short enough that a workgroup owns one 16-row weight tile they run on
+# the wave-private MFMA kernel, else on the shared-ring one.  Cases: fewer
+# chunks than waves, chunks that do not divide among the waves, a partial last
+# tile, partial and empty row tiles of a workgroup owning 24 or 36 rows, full
+# one-word tiles, and the residual epilogue.
 _WAVE_CASES = [(37, 256, 4, "i8x2", False), (1000, 2304, 7, "i8", True), (4000, 4096, 16, "i8", False),
-               (100, 8192, 8, "i8x2", True), (4096, 1024, 5, "i8x2", True), (4001, 14336, 8, "i8x2", False)]
+               (100, 8192, 8, "i8x2", True), (4096, 1024, 5, "i8x2", True), (4001, 14336, 8, "i8x2", False),
+               (9000, 4608, 8, "i8x2", True), (6000, 2048, 3, "i8", False), (14336, 4096, 6, "i8", True)]
 
 
 @pytest.mark.parametrize("n,k,rows,mode,with_res", _WAVE_CASES)
-def test_mma_wave_kernel(n, k, rows, mode, with_res):
-    say("mma wave kernel", n, k, rows, mode, with_res)
+def test_mma_single_tile_kernels(n, k, rows, mode, with_res):
+    say("mma single tile", n, k, rows, mode, with_res)
     w = synth.weights(n, k, seed=700 + n % 89)
     x = synth.activations(rows, k, seed=701 + rows)
     res = synth.normal(702, (rows, n)) if with_res else None
@@ -467,7 +471,7 @@ def test_mma_wave_kernel(n, k, rows, mode, with_res):
     torch.cuda.synchronize()
     ohi, olo, osc = oracle.quantize_act(mode, x)
     r, a = oracle.project(mode, blocks, n, k, rows, hi=ohi, lo=olo, scale=osc, residual=res)
-    gate(y.cpu().numpy(), r, a, f"mma wave {n}x{k} rows={rows} {mode}")
+    gate(y.cpu().numpy(), r, a, f"mma single tile {n}x{k} rows={rows} {mode}")
 
 
 # Every instantiation class of the MFMA kernel: a workgroup owns up to 16, 32 or
