@@ -624,9 +624,11 @@ bool mma_supports(int mode, int64_t n, int64_t k, int rows, const void *w, const
                   const void *scale) {
     if (mode != 1 && mode != 2) return false;
     if (rows < 2 || rows > 64 || k % (kChunkBlocks * kBlock) != 0) return false;
-    // Measured crossover with the GEMV: it is faster for two rows, and for three
-    // when the matrix is so short that a workgroup would own a single 16-row tile.
-    if (rows == 2 || (rows == 3 && n <= 16 * static_cast<int64_t>(device_info().cus))) return false;
+    // Measured crossover with the GEMV: it is faster for two rows, except in the
+    // two-word mode on a matrix short enough that a workgroup owns a single
+    // 16-row tile (the wave-private kernel).
+    const bool one_tile = n <= 16 * static_cast<int64_t>(device_info().cus);
+    if (rows == 2 && !(mode == 2 && one_tile)) return false;
     if (n * (k / kBlock) * kBlockBytes > (int64_t(1) << 30)) return false;
     const auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     if (!al16(w) || !al16(hi) || !al16(scale) || (mode == 2 && !al16(lo))) return false;
