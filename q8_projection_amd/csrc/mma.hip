@@ -377,10 +377,16 @@ __global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_kernel(MmaArgs a) {
 #pragma unroll
             for (int v = 0; v < L::kVals; ++v) acc[rt][t][v] = 0.0;
 
-    // Prologue: chunks 0 .. kDepth-2 in flight.
+    // Prologue: chunks 0 .. kDepth-2 in flight.  Chunk 0 goes out alone first,
+    // about half a microsecond ahead of the rest, so that the chip's first burst
+    // of requests serves every workgroup's first chunk before any second one
+    // (measured: 8 rows on 14336x4096, 16.6 -> 15.7 us; shorter or longer gaps
+    // gained less).
 #pragma unroll
-    for (int c = 0; c < L::kDepth - 1; ++c)
+    for (int c = 0; c < L::kDepth - 1; ++c) {
+        if (c == 1) __builtin_amdgcn_s_sleep(20);  // 20 x 64 clocks
         issue_chunk<RT, TT, WORDS, GR, GA, GB>(rs, plan, base + c * L::kSlotBytes, c, a.nchunks, wave);
+    }
 
     const bool more = wave < L::kCopies % W;  // this wave issues kPerWave copies per chunk, else kPerWaveLow
     int cur = 0;                 // slot of chunk c
