@@ -172,8 +172,9 @@ int64_t q8_argmax_workspace_bytes(int64_t n);
 /* The exact int32 block dot products of the integer modes, for checking:
  *   sums[r][n][b][0] = sum_j q[n][b][j] * hi[r][32b+j]
  *   sums[r][n][b][1] = sum_j q[n][b][j] * lo[r][32b+j]   (Q8_ACT_I8X2 only)
- * computed with the same device block decode and dot routine as the
- * projection kernels of rows <= 8.  sums: out, int32 [rows][n][k/32][words],
+ * computed with the same device block decode and dot routine as the GEMV
+ * projection kernels (the MFMA kernels' int32 sums are checked through their
+ * outputs).  sums: out, int32 [rows][n][k/32][words],
  * 4-byte aligned.  Errors as q8_matmul_rows (Q8_ACT_F32: Q8_E_MODE). */
 q8_status q8_block_sums(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
                         const int8_t *lo, int32_t *sums, void *stream);
