@@ -224,6 +224,91 @@ def time_head_argmax(p, reps):
             "pct_hbm_peak": round(c.weight_bytes / t / 1e9 / HBM_PEAK_GBPS * 100, 1), "index": want}
 
 
+def decode_layer_calls():
+    """The projections of one decode layer at rows=1, two-word, in the order a
+    step runs them: fused QKV (6144x4096: 32 query heads and 8 key/value heads
+    of 128), O (4096x4096) with the residual, gate and up (14336x4096, one
+    shared input), down (4096x14336) with the residual.  Synthetic weights
+    N(0, 0.02^2), activations and residuals N(0, 1)."""
+    from synth import workloads as wl
+    return [wl.Call("layer_qkv", 6144, 4096, 1, "i8x2", "matvec", w_seed=40, x_seed=41),
+            wl.Call("layer_o", 4096, 4096, 1, "i8x2", "matvec", w_seed=42, x_seed=43, residual_seed=44),
+            wl.Call("layer_gate", 14336, 4096, 1, "i8x2", "matvec", w_seed=45, x_seed=46),
+            wl.Call("layer_up", 14336, 4096, 1, "i8x2", "matvec", w_seed=47, x_seed=46),
+            wl.Call("layer_down", 4096, 14336, 1, "i8x2", "matvec", w_seed=48, x_seed=49, residual_seed=50)]
+
+
+def time_decode_layer(dev, iters):
+    """One decode layer's projections (decode_layer_calls), each input quantized
+    once (gate and up share theirs): nine kernels a layer.  Timed eagerly and as
+    a replayed HIP graph, alternating two copies of every matrix (463 MB, more
+    than the Infinity Cache); every replay must equal the eager layer."""
+    import torch
+    import q8_projection_amd as q8
+    calls = decode_layer_calls()
+    copies = 2
+    wts = []
+    for c in calls:
+        w = torch.from_numpy(c.make_weights()).to(dev)
+        wts.append([q8.quantize_weights(w) for _ in range(copies)])
+        del w
+    inputs = {}
+    for c in calls:
+        if c.x_seed not in inputs:
+            x = torch.from_numpy(c.make_activations()).to(dev)
+            inputs[c.x_seed] = (x, torch.empty((1, c.k), dtype=torch.int8, device=dev),
+                                torch.empty((1, c.k), dtype=torch.int8, device=dev),
+                                torch.empty((1, c.k // 32), dtype=torch.float32, device=dev))
+    res = [None if c.residual_seed is None else torch.from_numpy(c.make_residual()).to(dev) for c in calls]
+    ys = [torch.empty((1, c.n), dtype=torch.float32, device=dev) for c in calls]
+
+    def layer(copy):
+        done = set()
+        for i, c in enumerate(calls):
+            x, hi, lo, sc = inputs[c.x_seed]
+            if c.x_seed not in done:
+                q8.quantize_act("i8x2", x, hi=hi, lo=lo, scale=sc)
+                done.add(c.x_seed)
+            q8.matvec("i8x2", wts[i][copy], c.n, c.k, hi=hi[0], lo=lo[0], scale=sc[0],
+                      residual=None if res[i] is None else res[i][0], out=ys[i][0])
+
+    layer(0)
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in ys]
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(4):
+        layer(i % copies)
+    e0.record(s)
+    for i in range(iters):
+        layer(i % copies)
+    e1.record(s)
+    e1.synchronize()
+    eager = e0.elapsed_time(e1) / iters * 1e-3
+    graphs = [capture(lambda c=c: layer(c)) for c in range(copies)]
+    for g in graphs:
+        for y in ys:
+            y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(y, r) for y, r in zip(ys, ref)):
+            raise RuntimeError("decode-layer graph replay differs from the eager layer")
+    for i in range(4):
+        graphs[i % copies].replay()
+    e0.record(s)
+    for i in range(iters):
+        graphs[i % copies].replay()
+    e1.record(s)
+    e1.synchronize()
+    graph = e0.elapsed_time(e1) / iters * 1e-3
+    nbytes = sum(c.weight_bytes for c in calls)
+    return {"calls": [f"{c.name.split('_')[1]} {c.n}x{c.k}" + (" +res" if c.residual_seed is not None else "")
+                      for c in calls],
+            "kernels": 9, "weight_bytes": nbytes, "eager_us": round(eager * 1e6, 2),
+            "graph_us": round(graph * 1e6, 2), "GBps_graph": round(nbytes / graph / 1e9, 1),
+            "pct_hbm_peak_graph": round(nbytes / graph / 1e9 / HBM_PEAK_GBPS * 100, 1)}
+
+
 def capture(fn, reps=1):
     import torch
     g = torch.cuda.CUDAGraph()
@@ -398,6 +483,8 @@ def main(argv=None):
         del d["hbm_bytes_counted"]
     del others
     torch.cuda.empty_cache()
+    layer = time_decode_layer(dev, 50)
+    torch.cuda.empty_cache()
     by_rows = {}
     for name, d in per_call.items():
         key = str(d["rows"])
@@ -442,6 +529,7 @@ def main(argv=None):
         "per_call": per_call,
         "lm_head_argmax": head_argmax,
         "other_calls": other,
+        "decode_layer": layer,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -39,3 +39,12 @@ def test_counter_summary_is_keyed_on_its_sources(tmp_path, monkeypatch):
     src.write_text("kernel v2")
     assert bench.stored_traffic("demo") is None
     assert os.path.exists(tmp_path / "demo_counters.txt")
+
+
+def test_decode_layer_is_one_layers_projections():
+    calls = bench.decode_layer_calls()
+    assert [(c.n, c.k) for c in calls] == [(6144, 4096), (4096, 4096), (14336, 4096), (14336, 4096), (4096, 14336)]
+    assert all(c.rows == 1 and c.mode == "i8x2" for c in calls)
+    gate, up = calls[2], calls[3]
+    assert gate.x_seed == up.x_seed and gate.w_seed != up.w_seed
+    assert [c.residual_seed is not None for c in calls] == [False, True, False, False, True]
