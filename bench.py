@@ -238,11 +238,13 @@ def decode_layer_calls():
             wl.Call("layer_down", 4096, 14336, 1, "i8x2", "matvec", w_seed=48, x_seed=49, residual_seed=50)]
 
 
-def time_decode_layer(dev, iters):
+def time_decode_layer(dev, iters, inside=False):
     """One decode layer's projections (decode_layer_calls), each input quantized
-    once (gate and up share theirs): nine kernels a layer.  Timed eagerly and as
-    a replayed HIP graph, alternating two copies of every matrix (463 MB, more
-    than the Infinity Cache); every replay must equal the eager layer."""
+    once (gate and up share theirs): nine kernels a layer.  With `inside`, the
+    projections of 4096-column inputs take the f32 input and quantize it in
+    their own staging (six kernels).  Timed eagerly and as a replayed HIP
+    graph, alternating two copies of every matrix (463 MB, more than the
+    Infinity Cache); every replay must equal the eager layer."""
     import torch
     import q8_projection_amd as q8
     calls = decode_layer_calls()
@@ -266,6 +268,10 @@ def time_decode_layer(dev, iters):
         done = set()
         for i, c in enumerate(calls):
             x, hi, lo, sc = inputs[c.x_seed]
+            if inside and c.k <= 4096:
+                q8.matvec("i8x2", wts[i][copy], c.n, c.k, x=x[0],
+                          residual=None if res[i] is None else res[i][0], out=ys[i][0])
+                continue
             if c.x_seed not in done:
                 q8.quantize_act("i8x2", x, hi=hi, lo=lo, scale=sc)
                 done.add(c.x_seed)
@@ -304,7 +310,8 @@ def time_decode_layer(dev, iters):
     nbytes = sum(c.weight_bytes for c in calls)
     return {"calls": [f"{c.name.split('_')[1]} {c.n}x{c.k}" + (" +res" if c.residual_seed is not None else "")
                       for c in calls],
-            "kernels": 9, "weight_bytes": nbytes, "eager_us": round(eager * 1e6, 2),
+            "kernels": 6 if inside else 9, "quantize_inside": inside, "weight_bytes": nbytes,
+            "eager_us": round(eager * 1e6, 2),
             "graph_us": round(graph * 1e6, 2), "GBps_graph": round(nbytes / graph / 1e9, 1),
             "pct_hbm_peak_graph": round(nbytes / graph / 1e9 / HBM_PEAK_GBPS * 100, 1)}
 
@@ -485,6 +492,8 @@ def main(argv=None):
     torch.cuda.empty_cache()
     layer = time_decode_layer(dev, 50)
     torch.cuda.empty_cache()
+    layer_inside = time_decode_layer(dev, 50, inside=True)
+    torch.cuda.empty_cache()
     by_rows = {}
     for name, d in per_call.items():
         key = str(d["rows"])
@@ -530,6 +539,7 @@ def main(argv=None):
         "lm_head_argmax": head_argmax,
         "other_calls": other,
         "decode_layer": layer,
+        "decode_layer_quantize_inside": layer_inside,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
