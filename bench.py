@@ -368,28 +368,44 @@ def cpu_baseline(calls, budget_s: float):
         res_s = None if res is None else np.ascontiguousarray(res[:, rows_sel])
         work.append((c, blocks, x, res_s, rows_sel.size))
     sample_bytes = sum(n_s * (c.k // 32) * 34 for c, _, _, _, n_s in work)
-    times = []
-    t_end = time.perf_counter() + budget_s
-    while True:
-        t0 = time.perf_counter()
+
+    def one_pass():
         for c, blocks, x, res_s, n_s in work:
             if c.mode == "f32":
                 oracle.project(c.mode, blocks, n_s, c.k, x.shape[0], x=x, residual=res_s)
             else:
                 hi, lo, sc = oracle.quantize_act(c.mode, x)
                 oracle.project(c.mode, blocks, n_s, c.k, x.shape[0], hi=hi, lo=lo, scale=sc, residual=res_s)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() > t_end or len(times) >= 50:
-            break
-    med = sorted(times)[len(times) // 2]
+
+    def timed(seconds, max_passes):
+        one_pass()  # warm-up
+        times = []
+        t_end = time.perf_counter() + seconds
+        while True:
+            t0 = time.perf_counter()
+            one_pass()
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() > t_end or len(times) >= max_passes:
+                break
+        return sorted(times)[len(times) // 2], len(times)
+
+    all_threads = oracle.threads()
+    med, n_all = timed(budget_s, 5000)
+    oracle.set_threads(1)
+    try:
+        med1, n_one = timed(budget_s / 2, 500)
+    finally:
+        oracle.set_threads(all_threads)
     return {
         "value": round(sample_bytes / med / 1e9, 3),
         "unit": "GB/s",
-        "cores": oracle.threads(),
+        "cores": all_threads,
         "kind": "oracle",
+        "value_1thread": round(sample_bytes / med1 / 1e9, 3),
         "sample": f"every {stride}th weight row of each call of the step (full K, all activation rows), "
                   f"{sample_bytes / 1e6:.1f} MB of Q8_0 weights; activation quantization + projection; "
-                  f"median of {len(times)} passes",
+                  f"median of {n_all} passes on {all_threads} threads (value) and of {n_one} passes on one "
+                  f"thread (value_1thread), each after one warm-up pass",
     }
 
 
@@ -398,7 +414,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle timing on all threads (half as long again on one thread)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None, help="run only the named call eagerly (for profilers)")
     ap.add_argument("--sweep", default=None, metavar="N,K,MODE",

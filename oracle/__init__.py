@@ -59,6 +59,7 @@ def _load():
                                       _P, _P]),
             "q8ref_dense_matvec": (None, [_P, _I64, _I64, _I64, _P, _P]),
             "q8ref_threads": (_I, []),
+            "q8ref_set_threads": (None, [_I]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -71,6 +72,11 @@ def _load():
 def threads() -> int:
     """Threads the oracle's OpenMP loops use."""
     return int(_load().q8ref_threads())
+
+
+def set_threads(n: int) -> None:
+    """Use n threads in the oracle's OpenMP loops from now on."""
+    _load().q8ref_set_threads(int(n))
 
 
 def _ptr(a):

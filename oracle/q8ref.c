@@ -319,10 +319,13 @@ void q8ref_rha_array(const float *x, int64_t count, float *out) {
     for (int64_t i = 0; i < count; ++i) out[i] = rha(x[i]);
 }
 
-/* Threads the OpenMP loops above use. */
+/* Threads the OpenMP loops above use, and a way to change that (for timing the
+ * oracle on one thread and on all). */
 #ifdef _OPENMP
 #include <omp.h>
 int q8ref_threads(void) { return omp_get_max_threads(); }
+void q8ref_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int q8ref_threads(void) { return 1; }
+void q8ref_set_threads(int n) { (void)n; }
 #endif
