@@ -119,10 +119,12 @@ struct MmaArgs {
     int rows;                // activation rows (<= kActRows)
     int rows_per_wg;
     int nchunks;             // nb / 8
+    uint32_t lo_oob;         // kOob for a one-word stack run in the two-word layout, else 0
 };
 
 struct Rsrcs {
     __amdgpu_buffer_rsrc_t w, hi, lo, s;
+    uint32_t lo_oob;  // kOob: the lo words read as zeros (a one-word stack in the two-word layout)
 };
 
 // One direct-to-LDS copy: lane i's 16 bytes at buffer offset `off` land at LDS
@@ -215,7 +217,8 @@ __device__ __forceinline__ void issue_chunk(const Rsrcs &rs,
         } else if (i < L::kWCopies + L::kACopies) {
             // slots 0..7 hold hi rows, 8..15 lo rows; a copy fills kColsPerCopy of them
             const bool lo = WORDS == 2 && ((i - L::kWCopies) % kTileCopies) * kColsPerCopy >= 8;
-            copy16(lo ? rs.lo : rs.hi, slot + i * kCopyBytes, (base[u] + c * kActChunk) | chunk_oob);
+            copy16(lo ? rs.lo : rs.hi, slot + i * kCopyBytes,
+                   (base[u] + c * kActChunk) | chunk_oob | (lo ? rs.lo_oob : 0u));
         } else {
             copy4(rs.s, slot + L::kSOff + (i - L::kWCopies - L::kACopies) * 256,
                   (base[u] + c * (kChunkBlocks * 4)) | chunk_oob);
@@ -356,6 +359,7 @@ __global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_kernel(MmaArgs a) {
     rs.hi = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(a.hi), 0, act_bytes, kBufferDword3);
     rs.lo = WORDS == 2 ? __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(a.lo), 0, act_bytes, kBufferDword3)
                        : rs.hi;
+    rs.lo_oob = a.lo_oob;
     rs.s = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.scale), 0,
                                              static_cast<uint32_t>(a.rows) * a.nb * 4, kBufferDword3);
     const uint32_t base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((uintptr_t)(lds_ptr_t)smem));
@@ -509,6 +513,7 @@ __global__ __launch_bounds__(64 * W, 1) void mma_wave_kernel(MmaArgs a) {
     rs.hi = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(a.hi), 0, act_bytes, kBufferDword3);
     rs.lo = WORDS == 2 ? __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(a.lo), 0, act_bytes, kBufferDword3)
                        : rs.hi;
+    rs.lo_oob = a.lo_oob;
     rs.s = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.scale), 0,
                                              static_cast<uint32_t>(a.rows) * a.nb * 4, kBufferDword3);
     const uint8_t *ring = smem + wave * WL::kRing;
@@ -648,7 +653,12 @@ bool mma_supports(int mode, int64_t n, int64_t k, int rows, const void *w, const
 hipError_t launch_mma(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
                       const int8_t *lo, const float *scale, const float *residual, float *y, int64_t ldy,
                       hipStream_t stream) {
-    const int words = mode == 2 ? 2 : 1;
+    // One-word stacks of up to eight rows run in the two-word layout with their
+    // lo words read as zeros: T = 128 S_hi is exact, the final 1/128 undoes the
+    // factor (a power of two: the f64 sums carry the same bits scaled), and a
+    // lane rescales two rows per product instead of four.
+    const bool as_two_word = mode == 1 && rows <= 8;
+    const int words = mode == 2 || as_two_word ? 2 : 1;
     const int64_t nb = k / kBlock;
     const int at = act_tiles(words, rows);
     const int cus = std::max(1, device_info().cus);
@@ -658,7 +668,8 @@ hipError_t launch_mma(int mode, const uint8_t *w, int64_t n, int64_t k, int rows
     MmaArgs a;
     a.w = w;
     a.hi = hi;
-    a.lo = lo;
+    a.lo = as_two_word ? hi : lo;
+    a.lo_oob = as_two_word ? kOob : 0u;
     a.scale = scale;
     a.residual = residual;
     a.y = y;
