@@ -38,11 +38,11 @@ bool gemv_row_resident(int mode, int64_t k);
 hipError_t launch_mma(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
                       const int8_t *lo, const float *scale, const float *residual, float *y, int64_t ldy,
                       hipStream_t stream);
-// Whether launch_mma serves this call: integer mode, 3..64 rows (and two-word
-// stacks of 2 rows on a matrix of at most 16 rows per CU, or whose row ranges
-// fill at least three quarters of their MFMA tiles; the GEMV is faster for the
-// other 2-row stacks), k a multiple of 256, weights under 1 GiB, and weights,
-// words and scales 16-byte aligned.
+// Whether launch_mma serves this call: integer mode, 3..64 rows (and stacks of
+// 2 rows on a matrix of at most 16 rows per CU, or whose row ranges fill at
+// least three quarters of their MFMA tiles (two-word) or whole 64-row ranges
+// (one-word); the GEMV is faster for the other 2-row stacks), k a multiple of
+// 256, weights under 1 GiB, and weights, words and scales 16-byte aligned.
 bool mma_supports(int mode, int64_t n, int64_t k, int rows, const void *w, const void *hi, const void *lo,
                   const void *scale);
 

@@ -635,15 +635,17 @@ bool mma_supports(int mode, int64_t n, int64_t k, int rows, const void *w, const
                   const void *scale) {
     if (mode != 1 && mode != 2) return false;
     if (rows < 2 || rows > 64 || k % (kChunkBlocks * kBlock) != 0) return false;
-    // Measured crossover with the GEMV: it is faster for two rows, except in the
-    // two-word mode on a matrix short enough that a workgroup owns a single
-    // 16-row tile (the wave-private kernel) or whose workgroups fill at least
-    // three quarters of their 32- or 64-row tile range.
+    // Measured crossover with the GEMV at two rows: the MFMA kernels are faster
+    // on a matrix short enough that a workgroup owns a single 16-row tile (the
+    // wave-private kernel), and on taller ones where the workgroups fill at least
+    // three quarters of their 32- or 64-row tile range (two-word) or all 64 rows
+    // (one-word); elsewhere the GEMV is.
     const int64_t cus = std::max(1, device_info().cus);
     const int64_t per_wg = std::min<int64_t>((n + cus - 1) / cus, 64);
     const int64_t tile_rows = per_wg <= 16 ? 16 : per_wg <= 32 ? 32 : 64;
     const bool one_tile = per_wg <= 16;
-    if (rows == 2 && !(mode == 2 && (one_tile || 4 * per_wg >= 3 * tile_rows))) return false;
+    const bool two_rows = one_tile || (mode == 2 ? 4 * per_wg >= 3 * tile_rows : per_wg == 64);
+    if (rows == 2 && !two_rows) return false;
     if (n * (k / kBlock) * kBlockBytes > (int64_t(1) << 30)) return false;
     const auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     if (!al16(w) || !al16(hi) || !al16(scale) || (mode == 2 && !al16(lo))) return false;

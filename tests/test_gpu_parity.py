@@ -452,12 +452,15 @@ def test_host_mapped_weights_same_bits():
 # the wave-private MFMA kernel, else on the shared-ring one.  Cases: fewer
 # chunks than waves, chunks that do not divide among the waves, a partial last
 # tile, partial and empty row tiles of a workgroup owning 24 or 36 rows, full
-# one-word tiles, two- and three-row stacks, and the residual epilogue.
+# one-word tiles, one-word stacks of up to eight rows (run in the two-word
+# layout), two- and three-row stacks, and the residual epilogue.
 _WAVE_CASES = [(37, 256, 4, "i8x2", False), (1000, 2304, 7, "i8", True), (4000, 4096, 16, "i8", False),
                (100, 8192, 8, "i8x2", True), (4096, 1024, 5, "i8x2", True), (4001, 14336, 8, "i8x2", False),
                (9000, 4608, 8, "i8x2", True), (6000, 2048, 3, "i8", False), (14336, 4096, 6, "i8", True),
                (700, 2048, 2, "i8x2", True), (4096, 4096, 3, "i8x2", False), (2000, 1024, 3, "i8", True),
-               (14336, 4096, 2, "i8x2", True), (9000, 1024, 2, "i8x2", False), (7000, 1024, 2, "i8x2", True)]
+               (14336, 4096, 2, "i8x2", True), (9000, 1024, 2, "i8x2", False), (7000, 1024, 2, "i8x2", True),
+               (4096, 4096, 2, "i8", True), (20000, 2048, 2, "i8", False), (14336, 2048, 8, "i8", True),
+               (3000, 1024, 5, "i8", False)]
 
 
 @pytest.mark.parametrize("n,k,rows,mode,with_res", _WAVE_CASES)
