@@ -591,7 +591,8 @@ hipError_t run(const MmaArgs &a, hipStream_t stream) {
 }
 
 // Wave split per (weight tiles, activation tiles), measured.  One activation
-// tile and four weight tiles: two weight groups and four block groups.  Two
+// tile and four weight tiles: sixteen waves, one weight tile each, four block
+// groups (2-6% faster than two weight groups of eight waves).  Two
 // activation tiles and one weight tile: sixteen waves (eight block groups).
 // Eight activation tiles and four weight tiles: four tiles a wave and eight
 // block groups.  Otherwise one weight group and, by activation tiles: one tile,
@@ -603,7 +604,7 @@ struct Split {
     int gr, ga, gb;
 };
 constexpr Split wave_split(int rt, int tt) {
-    if (rt == 4 && tt == 1) return Split{2, 1, 4};
+    if (rt == 4 && tt == 1) return Split{4, 1, 4};
     if (rt == 4 && tt == 8) return Split{1, 2, 8};
     if (rt == 1 && tt == 2) return Split{1, 2, 8};
     return Split{1, tt <= 4 ? (tt == 1 ? 1 : 2) : 4, tt == 1 ? 8 : tt == 4 ? 8 : 4};
