@@ -598,12 +598,11 @@ hipError_t run(const MmaArgs &a, hipStream_t stream) {
 //    each, four block groups (5% faster than 1x2x4).
 //  - Two activation tiles and one weight tile: sixteen waves, eight block
 //    groups.
-//  - Eight activation tiles and four or one weight tiles: four tiles a wave,
-//    eight block groups (one weight tile: 6-7% faster than 1x4x4).
+//  - Eight activation tiles: four tiles a wave, eight block groups (with one
+//    or two weight tiles 5-7% faster than 1x4x4).
 //  - Otherwise one weight group and, by activation tiles: one tile, eight
 //    block groups; two, one tile a wave and four block groups; four, two tiles
-//    a wave and eight block groups; eight, two tiles a wave and four block
-//    groups.
+//    a wave and eight block groups.
 // Splitting the output tiles wider than this (fewer block groups, less operand
 // reuse per wave) measured slower.
 struct Split {
@@ -612,9 +611,9 @@ struct Split {
 constexpr Split wave_split(int rt, int tt) {
     if (rt == 4 && (tt == 1 || tt == 2)) return Split{4, 1, 4};
     if (rt == 2 && tt == 2) return Split{2, 2, 4};
-    if (tt == 8 && (rt == 4 || rt == 1)) return Split{1, 2, 8};
+    if (tt == 8) return Split{1, 2, 8};
     if (rt == 1 && tt == 2) return Split{1, 2, 8};
-    return Split{1, tt <= 4 ? (tt == 1 ? 1 : 2) : 4, tt == 1 ? 8 : tt == 4 ? 8 : 4};
+    return Split{1, tt == 1 ? 1 : 2, tt == 2 ? 4 : 8};
 }
 
 template <int WORDS, int TT, int RT>
