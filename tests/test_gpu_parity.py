@@ -460,7 +460,7 @@ _WAVE_CASES = [(37, 256, 4, "i8x2", False), (1000, 2304, 7, "i8", True), (4000, 
                (700, 2048, 2, "i8x2", True), (4096, 4096, 3, "i8x2", False), (2000, 1024, 3, "i8", True),
                (14336, 4096, 2, "i8x2", True), (9000, 1024, 2, "i8x2", False), (7000, 1024, 2, "i8x2", True),
                (4096, 4096, 2, "i8", True), (20000, 2048, 2, "i8", False), (14336, 2048, 8, "i8", True),
-               (3000, 1024, 5, "i8", False)]
+               (3000, 1024, 5, "i8", False), (1, 256, 2, "i8x2", True), (5, 256, 8, "i8", True)]
 
 
 @pytest.mark.parametrize("n,k,rows,mode,with_res", _WAVE_CASES)
