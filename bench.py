@@ -439,13 +439,14 @@ def main(argv=None):
     if args.sweep:
         sweep(args.sweep, dev)
         return 0
-    calls = step_calls()
-    copies = 2  # the step graphs alternate two copies of every matrix
-    prepared = [Prepared(c, dev) for c in calls]
-    torch.cuda.synchronize()
-
     if args.only:
-        p = next(p for p in prepared if p.call.name == args.only)
+        from synth import workloads as wl
+        by_name = {c.name: c for c in wl.all_calls()}
+        if args.only not in by_name:
+            print(f"--only: no call named {args.only!r}; calls: {', '.join(by_name)}", file=sys.stderr)
+            return 2
+        p = Prepared(by_name[args.only], dev)
+        torch.cuda.synchronize()
         p.quantize()
         for i in range(args.warmup + args.steps):
             p.project(i % p.copies)
@@ -463,6 +464,11 @@ def main(argv=None):
         print(json.dumps({"only": args.only, "launches": args.warmup + args.steps,
                           "weight_bytes_per_launch": p.call.weight_bytes, "calib_copy_bytes_each": copied // 4}))
         return 0
+
+    calls = step_calls()
+    copies = 2  # the step graphs alternate two copies of every matrix
+    prepared = [Prepared(c, dev) for c in calls]
+    torch.cuda.synchronize()
 
     def step(copy):
         for p in prepared:

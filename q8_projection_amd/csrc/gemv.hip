@@ -932,18 +932,26 @@ hipError_t run(GemvArgs a, hipStream_t stream) {
         const DeviceInfo dev = device_info();
         // enough waves to fill the chip, and enough that none parks more than
         // kOutPerWave totals
-        const int64_t groups_cap = kOutPerWave / (MR * R);
-        const int64_t min_waves = (a.num_groups + groups_cap - 1) / groups_cap;
-        int64_t waves = std::min<int64_t>(a.num_groups, static_cast<int64_t>(dev.cus) * kWavesPerCu);
-        waves = std::max<int64_t>(waves, min_waves);
-        const int64_t grid = (waves + kWaves - 1) / kWaves;
-        const size_t lds = ((stack + 15) & ~size_t(15)) + static_cast<size_t>(kWaves) * kOutPerWave * 8;
         // the ring kernel stages the stack in whole 2048-column parts
         const int kt_ring = (a.k + kPartCols - 1) / kPartCols * kPartCols;
         const size_t ring_lds =
             ring_lds_offset(R, WORDS, kt_ring) + static_cast<size_t>(kWaves) * P * MR * kSlotBytes;
         const bool aligned = (row_bytes % 16) == 0 && (reinterpret_cast<uintptr_t>(a.w) & 15) == 0;
-        if (aligned && ring_lds * 2 <= static_cast<size_t>(dev.lds_per_block)) {
+        const size_t cu_lds = static_cast<size_t>(dev.lds_per_block);
+        const bool ring = aligned && ring_lds * 2 <= cu_lds;
+        // The f32 mode's f64 math leaves the SIMDs half idle at two waves each:
+        // where three of its workgroups fit a CU it runs 12 waves a CU
+        // (measured at 14336x4096: 17.6-18.7 -> 16.1-16.3 us; 16 waves were
+        // slower than 12).  Not with the fused arg-max, whose workspace is
+        // sized for the 8-wave grid.
+        const int per_cu = (WORDS == 0 && ring && !a.argmax && ring_lds * 3 <= cu_lds) ? 12 : kWavesPerCu;
+        const int64_t groups_cap = kOutPerWave / (MR * R);
+        const int64_t min_waves = (a.num_groups + groups_cap - 1) / groups_cap;
+        int64_t waves = std::min<int64_t>(a.num_groups, static_cast<int64_t>(dev.cus) * per_cu);
+        waves = std::max<int64_t>(waves, min_waves);
+        const int64_t grid = (waves + kWaves - 1) / kWaves;
+        const size_t lds = ((stack + 15) & ~size_t(15)) + static_cast<size_t>(kWaves) * kOutPerWave * 8;
+        if (ring) {
             GemvArgs b = a;
             b.kt = kt_ring;
             const dim3 g(static_cast<unsigned>(grid));
