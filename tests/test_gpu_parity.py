@@ -501,3 +501,26 @@ def test_mma_instantiations(n, rows, mode):
     ohi, olo, osc = oracle.quantize_act(mode, x)
     r, a = oracle.project(mode, blocks, n, k, rows, hi=ohi, lo=olo, scale=osc)
     gate(y.cpu().numpy(), r, a, f"mma {n}x{k} rows={rows} {mode}")
+
+
+@pytest.mark.parametrize("n,k,with_res", [(5000, 2304, True), (777, 6912, False), (3072, 4352, True),
+                                          (100, 256, True), (14336, 6144, False), (50, 8192, True)])
+def test_f32_row_on_both_grids(n, k, with_res):
+    """The f32 mode at one row runs 12 waves a CU where three workgroups fit
+    (k up to 6144, ragged k included), and the fused arg-max keeps the 8-wave
+    grid.  Every row's total is one wave's, in the same order on either grid,
+    so y is the same bits both ways; and it meets the oracle's gate."""
+    say("f32 one row, both grids", n, k, with_res)
+    w = synth.weights(n, k, seed=2100 + n % 89, outlier_frac=0.01)
+    x = synth.activations(1, k, seed=2200 + k, outlier_frac=0.005)[0]
+    res = synth.normal(2300, (n,)) if with_res else None
+    blocks = oracle.quantize_weights(w)
+    wd, xd = to_dev(blocks), to_dev(x)
+    rd = None if res is None else to_dev(res)
+    y = q8.matvec("f32", wd, n, k, x=xd, residual=rd)
+    work = torch.zeros(q8.argmax_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    y8, _ = q8.matvec_argmax("f32", wd, n, k, x=xd, residual=rd, workspace=work)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y8)
+    r, a = oracle.project("f32", blocks, n, k, 1, x=x[None], residual=None if res is None else res[None])
+    gate(y.cpu().numpy()[None], r, a, f"f32 {n}x{k}")
