@@ -225,17 +225,9 @@ def time_head_argmax(p, reps):
 
 
 def decode_layer_calls():
-    """The projections of one decode layer at rows=1, two-word, in the order a
-    step runs them: fused QKV (6144x4096: 32 query heads and 8 key/value heads
-    of 128), O (4096x4096) with the residual, gate and up (14336x4096, one
-    shared input), down (4096x14336) with the residual.  Synthetic weights
-    N(0, 0.02^2), activations and residuals N(0, 1)."""
+    """The projections of one decode layer (synth.workloads.decode_layer)."""
     from synth import workloads as wl
-    return [wl.Call("layer_qkv", 6144, 4096, 1, "i8x2", "matvec", w_seed=40, x_seed=41),
-            wl.Call("layer_o", 4096, 4096, 1, "i8x2", "matvec", w_seed=42, x_seed=43, residual_seed=44),
-            wl.Call("layer_gate", 14336, 4096, 1, "i8x2", "matvec", w_seed=45, x_seed=46),
-            wl.Call("layer_up", 14336, 4096, 1, "i8x2", "matvec", w_seed=47, x_seed=46),
-            wl.Call("layer_down", 4096, 14336, 1, "i8x2", "matvec", w_seed=48, x_seed=49, residual_seed=50)]
+    return wl.decode_layer()
 
 
 def time_decode_layer(dev, iters, inside=False):
@@ -316,6 +308,23 @@ def time_decode_layer(dev, iters, inside=False):
             "pct_hbm_peak_graph": round(nbytes / graph / 1e9 / HBM_PEAK_GBPS * 100, 1)}
 
 
+def rows_summary(per_call, ceiling):
+    """The metric's rows=1/8/64 figures, each on its own shapes: rows=1 is the
+    4096x14336 down projection alone (the LM head, also one row, has an entry
+    of its own), rows=8 the two batched calls together, rows=64 the prefill."""
+    groups = {"1": ["down_i8x2"], "8": ["batch8", "batch8_down_res"], "64": ["prefill64"],
+              "lm_head": ["lm_head"]}
+    out = {}
+    for key, names in groups.items():
+        nbytes = sum(per_call[n]["weight_bytes"] for n in names)
+        us = sum(per_call[n]["project_us"] for n in names)
+        ceil_us = sum(ceiling[str(per_call[n]["weight_bytes"])]["us"] for n in names)
+        gbps = nbytes / us / 1e3
+        out[key] = {"calls": names, "GBps": round(gbps, 1), "pct_hbm_peak": round(gbps / HBM_PEAK_GBPS * 100, 1),
+                    "pct_of_stream_ceiling": round(ceil_us / us * 100, 1)}
+    return out
+
+
 def capture(fn, reps=1):
     import torch
     g = torch.cuda.CUDAGraph()
@@ -345,6 +354,55 @@ def time_graph(g, iters):
     e1.record(s)
     e1.synchronize()
     return e0.elapsed_time(e1) / iters * 1e-3  # seconds
+
+
+def stream_ceiling(sizes, dev, reps=20):
+    """The measured streaming-read ceiling for each byte count: the bare read
+    of libq8probe.so (no math, the GEMV's copy form and ring), over rotating
+    buffers like the projections' weight copies, best over its ring depths and
+    occupancies.  Time per launch from graphs of `reps` launches."""
+    import ctypes
+    import torch
+    from q8_projection_amd import build as q8build
+    if not os.path.exists(q8build.PROBE_LIB):
+        raise ImportError(f"{q8build.PROBE_LIB} is missing: build it with q8_projection_amd/build.py")
+    lib = ctypes.CDLL(q8build.PROBE_LIB)
+    lib.q8probe_stream.restype = ctypes.c_int
+    lib.q8probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    out = {}
+    for size in sorted(set(sizes)):
+        copies = max(2, -(-(512 << 20) // size))
+        bufs = [torch.empty(size, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        best = None
+        for ring in (2, 4, 8):
+            for wpc in (8, 16):
+                def launch(i, ring=ring, wpc=wpc):
+                    rc = lib.q8probe_stream(ctypes.c_void_p(bufs[i % copies].data_ptr()), size, ring, wpc,
+                                            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                    if rc != 0:
+                        raise RuntimeError(f"q8probe_stream: {rc}")
+                g = capture(lambda: [launch(i) for i in range(reps)])
+                t = time_graph(g, 5) / reps
+                if best is None or t < best[0]:
+                    best = (t, ring, wpc)
+        del bufs
+        torch.cuda.empty_cache()
+        t, ring, wpc = best
+        out[str(size)] = {"us": round(t * 1e6, 3), "GBps": round(size / t / 1e9, 1),
+                          "pct_hbm_peak": round(size / t / 1e9 / HBM_PEAK_GBPS * 100, 1),
+                          "ring": ring, "waves_per_cu": wpc, "buffers": copies}
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(calls, budget_s: float):
@@ -400,6 +458,7 @@ def cpu_baseline(calls, budget_s: float):
         "value": round(sample_bytes / med / 1e9, 3),
         "unit": "GB/s",
         "cores": all_threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "value_1thread": round(sample_bytes / med1 / 1e9, 3),
         "sample": f"every {stride}th weight row of each call of the step (full K, all activation rows), "
@@ -517,24 +576,25 @@ def main(argv=None):
     torch.cuda.empty_cache()
     layer_inside = time_decode_layer(dev, 50, inside=True)
     torch.cuda.empty_cache()
-    by_rows = {}
-    for name, d in per_call.items():
-        key = str(d["rows"])
-        agg = by_rows.setdefault(key, {"bytes": 0, "us": 0.0})
-        agg["bytes"] += d["weight_bytes"]
-        agg["us"] += d["project_us"]
-    per_rows = {k: {"GBps": round(v["bytes"] / v["us"] / 1e3, 1),
-                    "pct_hbm_peak": round(v["bytes"] / v["us"] / 1e3 / HBM_PEAK_GBPS * 100, 1)}
-                for k, v in by_rows.items()}
+    ceiling = stream_ceiling([d["weight_bytes"] for d in per_call.values()] +
+                             [d["weight_bytes"] for d in other.values()], dev)
+    torch.cuda.empty_cache()
+    for d in list(per_call.values()) + list(other.values()):
+        c = ceiling[str(d["weight_bytes"])]
+        d["pct_of_stream_ceiling"] = round(c["us"] / d["project_us"] * 100, 1)
+    per_rows = rows_summary(per_call, ceiling)
 
     dom_name = max(per_call, key=lambda n: per_call[n]["project_us"])
     dom = per_call[dom_name]
     achieved = dom["weight_bytes"] / (dom["project_us"] * 1e-6) / 1e9
     traffic = stored_traffic(dom_name)
+    dom_ceiling = ceiling[str(dom["weight_bytes"])]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": f"{dom_name}: rows={dom['rows']} {dom['n']}x{dom['k']} {dom['mode']}",
-                "algorithmic_bytes": dom["weight_bytes"]}
+                "algorithmic_bytes": dom["weight_bytes"],
+                "stream_ceiling_GBps": dom_ceiling["GBps"],
+                "frac_of_stream_ceiling": round(achieved / dom_ceiling["GBps"], 4)}
 
     cpu = None if args.no_cpu else cpu_baseline(calls, args.cpu_budget)
 
@@ -561,6 +621,7 @@ def main(argv=None):
         "per_call": per_call,
         "lm_head_argmax": head_argmax,
         "other_calls": other,
+        "stream_ceiling": ceiling,
         "decode_layer": layer,
         "decode_layer_quantize_inside": layer_inside,
         "roofline": roofline,

@@ -18,7 +18,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "q8ref.c")
-_LIB_PATH = os.path.join(_HERE, "libq8ref.so")
+# Q8REF_LIB names another build of the same source (the tests' sanitizer runs).
+_BUILT = os.path.join(_HERE, "libq8ref.so")
+_LIB_PATH = os.environ.get("Q8REF_LIB") or _BUILT
 _lib = None
 
 MODE = {"f32": 0, "i8": 1, "i8x2": 2}
@@ -34,9 +36,9 @@ def build() -> str:
     """Compile ``libq8ref.so`` (always recompiles).  Plain -O2, contraction off,
     no fast-math."""
     cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-           "-shared", "-fPIC", "-o", _LIB_PATH, _SRC, "-lm"]
+           "-shared", "-fPIC", "-o", _BUILT, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    return _LIB_PATH
+    return _BUILT
 
 
 def _load():

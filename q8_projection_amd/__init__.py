@@ -17,7 +17,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libq8proj.so")
+# Q8PROJ_LIB names another build of the same sources (the tests' host-sanitizer run).
+LIB_PATH = os.environ.get("Q8PROJ_LIB") or os.path.join(_HERE, "libq8proj.so")
 
 MODES = {"f32": 0, "i8": 1, "i8x2": 2}
 STATUS = {0: "Q8_OK", 1: "Q8_E_NULL", 2: "Q8_E_SHAPE", 3: "Q8_E_ALIGN", 4: "Q8_E_MODE",
@@ -96,6 +97,41 @@ def _check(fn: str, status: int):
         raise Q8Error(fn, status)
 
 
+def _want(t, name: str, dtype, numel: int, optional: bool = False):
+    """Raise ValueError unless t is a contiguous device tensor of `dtype` with at
+    least `numel` elements (or None where the argument is optional): the library
+    reads or writes that many elements from the pointer it is given."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, {numel} needed")
+
+
+def _want_weights(w, n: int, k: int):
+    _want(w, "w", torch.uint8, n * (k // BLOCK) * BLOCK_BYTES)
+
+
+def _want_stack(m: int, rows: int, k: int, hi, lo, scale, x):
+    """The activation arguments of a projection: the quantized stack (hi, lo,
+    scale) or, in the f32 mode or to quantize inside the call, x."""
+    if m == 0 or (hi is None and lo is None and scale is None):
+        _want(x, "x", torch.float32, rows * k)
+        return
+    _want(hi, "hi", torch.int8, rows * k)
+    _want(lo, "lo", torch.int8, rows * k, optional=m != 2)
+    _want(scale, "scale", torch.float32, rows * (k // BLOCK))
+
+
 def _device_of(*ts):
     for t in ts:
         if t is not None:
@@ -106,8 +142,10 @@ def _device_of(*ts):
 def quantize_weights(w: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Q8_0 blocks (uint8 [n][k/32*34]) of an f32 [n][k] matrix."""
     n, k = w.shape
+    _want(w, "w", torch.float32, n * k)
     if out is None:
         out = torch.empty((n, (k // BLOCK) * BLOCK_BYTES), dtype=torch.uint8, device=w.device)
+    _want(out, "out", torch.uint8, n * (k // BLOCK) * BLOCK_BYTES)
     _check("q8_quantize_weights", lib().q8_quantize_weights(_ptr(w), n, k, _ptr(out), _stream(stream)))
     return out
 
@@ -118,6 +156,7 @@ def quantize_act(mode, x: torch.Tensor, hi=None, lo=None, scale=None, stream=Non
     m = _mode(mode)
     x2 = x if x.dim() == 2 else x.view(1, -1)
     rows, k = x2.shape
+    _want(x2, "x", torch.float32, rows * k)
     dev = x.device
     if hi is None:
         hi = torch.empty((rows, k), dtype=torch.int8, device=dev)
@@ -125,6 +164,9 @@ def quantize_act(mode, x: torch.Tensor, hi=None, lo=None, scale=None, stream=Non
         lo = torch.empty((rows, k), dtype=torch.int8, device=dev)
     if scale is None:
         scale = torch.empty((rows, k // BLOCK), dtype=torch.float32, device=dev)
+    _want(hi, "hi", torch.int8, rows * k)
+    _want(lo, "lo", torch.int8, rows * k, optional=m != 2)
+    _want(scale, "scale", torch.float32, rows * (k // BLOCK))
     _check("q8_quantize_act", lib().q8_quantize_act(m, _ptr(x2), rows, k, _ptr(hi),
                                                     _ptr(lo if m == 2 else None), _ptr(scale),
                                                     _stream(stream)))
@@ -141,6 +183,10 @@ def matmul_rows(mode, w: torch.Tensor, n: int, k: int, hi=None, lo=None, scale=N
         rows = 1 if src is None or src.dim() == 1 else src.shape[0]
     if out is None:
         out = torch.empty((rows, n), dtype=torch.float32, device=_device_of(w, src))
+    _want_weights(w, n, k)
+    _want_stack(m, rows, k, hi, lo, scale, x)
+    _want(residual, "residual", torch.float32, rows * n, optional=True)
+    _want(out, "out", torch.float32, rows * n)
     _check("q8_matmul_rows", lib().q8_matmul_rows(m, _ptr(w), n, k, rows, _ptr(hi), _ptr(lo), _ptr(scale),
                                                   _ptr(x), _ptr(residual), _ptr(out), _stream(stream)))
     return out
@@ -152,6 +198,10 @@ def matvec(mode, w: torch.Tensor, n: int, k: int, hi=None, lo=None, scale=None, 
     m = _mode(mode)
     if out is None:
         out = torch.empty((n,), dtype=torch.float32, device=_device_of(w, hi, x))
+    _want_weights(w, n, k)
+    _want_stack(m, 1, k, hi, lo, scale, x)
+    _want(residual, "residual", torch.float32, n, optional=True)
+    _want(out, "out", torch.float32, n)
     _check("q8_matvec", lib().q8_matvec(m, _ptr(w), n, k, _ptr(hi), _ptr(lo), _ptr(scale), _ptr(x),
                                         _ptr(residual), _ptr(out), _stream(stream)))
     return out
@@ -176,6 +226,12 @@ def matvec_argmax(mode, w: torch.Tensor, n: int, k: int, hi=None, lo=None, scale
         idx = torch.empty((1,), dtype=torch.int32, device=dev)
     if workspace is None:
         workspace = torch.zeros(max(16, argmax_workspace_bytes(n)), dtype=torch.uint8, device=dev)
+    _want_weights(w, n, k)
+    _want_stack(m, 1, k, hi, lo, scale, x)
+    _want(residual, "residual", torch.float32, n, optional=True)
+    _want(out, "out", torch.float32, n)
+    _want(idx, "idx", torch.int32, 1)
+    _want(workspace, "workspace", torch.uint8, argmax_workspace_bytes(n))
     _check("q8_matvec_argmax", lib().q8_matvec_argmax(m, _ptr(w), n, k, _ptr(hi), _ptr(lo), _ptr(scale), _ptr(x),
                                                       _ptr(residual), _ptr(out), _ptr(idx), _ptr(workspace),
                                                       _stream(stream)))
@@ -191,6 +247,10 @@ def block_sums(mode, w: torch.Tensor, n: int, k: int, hi, lo=None, out=None, row
     words = 2 if m == 2 else 1
     if out is None:
         out = torch.empty((rows, n, k // BLOCK, words), dtype=torch.int32, device=hi.device)
+    _want_weights(w, n, k)
+    _want(hi, "hi", torch.int8, rows * k)
+    _want(lo, "lo", torch.int8, rows * k, optional=m != 2)
+    _want(out, "out", torch.int32, rows * n * (k // BLOCK) * words)
     _check("q8_block_sums", lib().q8_block_sums(m, _ptr(w), n, k, rows, _ptr(hi), _ptr(lo), _ptr(out),
                                                 _stream(stream)))
     return out

@@ -33,6 +33,18 @@ q8_status check_k(int64_t k) {
     return Q8_OK;
 }
 
+// Sizes of a projection, each bounded before any product of them is formed:
+// n * k/32 <= kMaxBlocks, rows * n <= kMaxRowsTimesN and rows <= 2^25, so
+// every byte count below fits int64 with room to spare.
+q8_status check_sizes(int64_t n, int64_t k, int64_t rows) {
+    if (n < 0 || rows < 0) return Q8_E_SHAPE;
+    if (q8_status s = check_k(k); s != Q8_OK) return s;
+    if (n > kMaxBlocks / (k / 32)) return Q8_E_SHAPE;
+    if (rows > kMaxRowsTimesN / 64) return Q8_E_SHAPE;
+    if (n > 0 && rows > kMaxRowsTimesN / n) return Q8_E_SHAPE;
+    return Q8_OK;
+}
+
 q8_status from_hip(hipError_t e) { return e == hipSuccess ? Q8_OK : Q8_E_HIP; }
 
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
@@ -43,10 +55,8 @@ q8_status check_projection(int mode, const void *w, int64_t n, int64_t k, int64_
                            const void *out, int64_t out_bytes, bool f32_allowed, bool need_scale) {
     if (mode != Q8_ACT_F32 && mode != Q8_ACT_I8 && mode != Q8_ACT_I8X2) return Q8_E_MODE;
     if (mode == Q8_ACT_F32 && !f32_allowed) return Q8_E_MODE;
-    if (n < 0 || rows < 0) return Q8_E_SHAPE;
-    if (q8_status s = check_k(k); s != Q8_OK) return s;
+    if (q8_status s = check_sizes(n, k, rows); s != Q8_OK) return s;
     const int64_t nb = k / 32;
-    if (n > kMaxBlocks / nb || rows * n > kMaxRowsTimesN || rows > kMaxRowsTimesN / 64) return Q8_E_SHAPE;
     if (!w || !out) return Q8_E_NULL;
     // Integer modes take the quantized stack (hi, lo, scale) or, with all three
     // null, the f32 stack x to quantize inside the projection.
@@ -77,6 +87,14 @@ q8_status check_projection(int mode, const void *w, int64_t n, int64_t k, int64_
     }
     if (residual && residual != out && overlap(out, out_bytes, residual, rows * n * 4)) return Q8_E_ALIAS;
     return Q8_OK;
+}
+
+// Which kernel family projects a slice of at most 64 rows.  The projection and
+// the block-sum export both ask here, so the export runs the projection's
+// kernels.
+bool mma_serves(int mode, int64_t n, int64_t k, int rows, const void *w, const int8_t *hi, const int8_t *lo,
+                const void *scale, bool quantize_inside) {
+    return !quantize_inside && q8::mma_supports(mode, n, k, rows, w, hi, lo, scale);
 }
 
 }  // namespace
@@ -138,6 +156,7 @@ q8_status q8_quantize_act(int mode, const float *x, int64_t rows, int64_t k, int
 q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
                          const int8_t *lo, const float *scale, const float *x, const float *residual,
                          float *y, void *stream) {
+    if (q8_status s = check_sizes(n, k, rows); s != Q8_OK) return s;  // before rows * n is formed
     if (q8_status s = check_projection(mode, w, n, k, rows, hi, lo, scale, x, residual, y, rows * n * 4, true, true);
         s != Q8_OK)
         return s;
@@ -156,7 +175,7 @@ q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t 
         const float *sres = residual ? residual + r0 * n : nullptr;
         float *sy = y + r0 * n;
         hipError_t e;
-        if (!inside && q8::mma_supports(mode, n, k, r, wb, shi, slo, ssc)) {
+        if (mma_serves(mode, n, k, r, wb, shi, slo, ssc, inside)) {
             e = q8::launch_mma(mode, wb, n, k, r, shi, slo, ssc, sres, sy, n, st);
         } else {
             // the GEMV family, 8 rows at a time
@@ -186,6 +205,7 @@ int64_t q8_argmax_workspace_bytes(int64_t n) {
 q8_status q8_matvec_argmax(int mode, const void *w, int64_t n, int64_t k, const int8_t *hi, const int8_t *lo,
                            const float *scale, const float *x, const float *residual, float *y, int32_t *idx,
                            void *workspace, void *stream) {
+    if (q8_status s = check_sizes(n, k, 1); s != Q8_OK) return s;  // before n * 4 is formed
     if (q8_status s = check_projection(mode, w, n, k, 1, hi, lo, scale, x, residual, y, n * 4, true, true);
         s != Q8_OK)
         return s;
@@ -216,15 +236,39 @@ q8_status q8_matvec_argmax(int mode, const void *w, int64_t n, int64_t k, const 
 
 q8_status q8_block_sums(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
                         const int8_t *lo, int32_t *sums, void *stream) {
+    if (mode != Q8_ACT_I8 && mode != Q8_ACT_I8X2) return Q8_E_MODE;
+    if (q8_status s = check_sizes(n, k, rows); s != Q8_OK) return s;
     const int words = mode == Q8_ACT_I8X2 ? 2 : 1;
-    const int64_t out_bytes = (k > 0 && k % 64 == 0) ? rows * n * (k / 32) * words * 4 : 0;
+    const int64_t nb = k / 32;
+    const int64_t out_bytes = rows * n * nb * words * 4;
     if (q8_status s = check_projection(mode, w, n, k, rows, hi, lo, nullptr, nullptr, nullptr, sums, out_bytes,
                                        false, false);
         s != Q8_OK)
         return s;
     if (n == 0 || rows == 0) return Q8_OK;
-    return from_hip(q8::launch_block_sums(words, static_cast<const uint8_t *>(w), n, k, rows, hi,
-                                          mode == Q8_ACT_I8X2 ? lo : nullptr, sums, as_stream(stream)));
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const hipStream_t st = as_stream(stream);
+    // the slices and kernels q8_matmul_rows would run on this stack (the
+    // scales, which the export does not take, counted as 16-byte aligned)
+    for (int64_t r0 = 0; r0 < rows; r0 += 64) {
+        const int r = static_cast<int>(std::min<int64_t>(64, rows - r0));
+        const int8_t *shi = hi + r0 * k;
+        const int8_t *slo = mode == Q8_ACT_I8X2 ? lo + r0 * k : nullptr;
+        int32_t *ssums = sums + r0 * n * nb * words;
+        hipError_t e;
+        if (mma_serves(mode, n, k, r, wb, shi, slo, shi, false)) {
+            e = q8::launch_mma_sums(mode, wb, n, k, r, shi, slo, ssums, st);
+        } else {
+            e = hipSuccess;
+            for (int c0 = 0; c0 < r && e == hipSuccess; c0 += 8) {
+                const int c = std::min(8, r - c0);
+                e = q8::launch_gemv_sums(words, wb, n, k, c, shi + c0 * k, slo ? slo + c0 * k : nullptr,
+                                         ssums + c0 * n * nb * words, n, st);
+            }
+        }
+        if (e != hipSuccess) return Q8_E_HIP;
+    }
+    return Q8_OK;
 }
 
 const char *q8_status_name(int status) {

@@ -33,11 +33,22 @@ int64_t gemv_row_grid(int64_t n);
 // (a single launch that can finish with the fused arg-max).
 bool gemv_row_resident(int mode, int64_t k);
 
+// The block sums of the integer modes as the GEMV kernel that would project
+// this call computes them (words 1 or 2, rows 1..8): sums [rows][sums_ld][k/32]
+// [words], this launch's n weight rows starting at row 0 of the export.
+hipError_t launch_gemv_sums(int words, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
+                            const int8_t *lo, int32_t *sums, int64_t sums_ld, hipStream_t stream);
+
 // Projection of 2..64 rows with the LDS-staged int8 MFMA kernel (integer
 // modes).  y and residual have row stride ldy.
 hipError_t launch_mma(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
                       const int8_t *lo, const float *scale, const float *residual, float *y, int64_t ldy,
                       hipStream_t stream);
+// The block sums of the same call as the MFMA kernel that launch_mma picks
+// computes them: sums [rows][n][k/32][words] (words 2 in the two-word mode).
+// Needs what mma_supports needs, with hi standing in for the scales.
+hipError_t launch_mma_sums(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
+                           const int8_t *lo, int32_t *sums, hipStream_t stream);
 // Whether launch_mma serves this call: integer mode, 3..64 rows (and stacks of
 // 2 rows on a matrix of at most 16 rows per CU, or whose row ranges fill at
 // least three quarters of their MFMA tiles (two-word) or whole 64-row ranges
@@ -46,7 +57,10 @@ hipError_t launch_mma(int mode, const uint8_t *w, int64_t n, int64_t k, int rows
 bool mma_supports(int mode, int64_t n, int64_t k, int rows, const void *w, const void *hi, const void *lo,
                   const void *scale);
 
+// One thread per weight block: the block sums as the resident and tiled GEMV
+// kernels form them (sums row stride sums_ld weight rows).
 hipError_t launch_block_sums(int words, const uint8_t *w, int64_t n, int64_t k, int64_t rows,
-                             const int8_t *hi, const int8_t *lo, int32_t *sums, hipStream_t stream);
+                             const int8_t *hi, const int8_t *lo, int32_t *sums, int64_t sums_ld,
+                             hipStream_t stream);
 
 }  // namespace q8

@@ -15,15 +15,17 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
-_LIB_PATH = os.path.join(_HERE, "libsynth.so")
+# SYNTH_LIB names another build of the same source (the tests' sanitizer runs).
+_BUILT = os.path.join(_HERE, "libsynth.so")
+_LIB_PATH = os.environ.get("SYNTH_LIB") or _BUILT
 _lib = None
 
 
 def build() -> str:
     """Compile ``libsynth.so`` next to its source (always recompiles)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", "-o", _LIB_PATH, _SRC, "-lm"]
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", "-o", _BUILT, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    return _LIB_PATH
+    return _BUILT
 
 
 def _load():

@@ -123,6 +123,20 @@ def prefill():
     ]
 
 
+def decode_layer():
+    """The projections of one decode layer at one row, two-word, in the order a
+    decode step runs them (model::author page, Functions: decode_layer): fused
+    QKV 6144x4096 (32 query heads and 8 key/value heads of 128 columns), O
+    4096x4096 with the residual, gate and up 14336x4096 on one shared input,
+    down 4096x14336 with the residual.  Not one of the parity workloads above:
+    the graph test and the benchmark's decode-layer figure use it."""
+    return [Call("layer_qkv", 6144, 4096, 1, "i8x2", "matvec", w_seed=40, x_seed=41),
+            Call("layer_o", 4096, 4096, 1, "i8x2", "matvec", w_seed=42, x_seed=43, residual_seed=44),
+            Call("layer_gate", 14336, 4096, 1, "i8x2", "matvec", w_seed=45, x_seed=46),
+            Call("layer_up", 14336, 4096, 1, "i8x2", "matvec", w_seed=47, x_seed=46),
+            Call("layer_down", 4096, 14336, 1, "i8x2", "matvec", w_seed=48, x_seed=49, residual_seed=50)]
+
+
 WORKLOADS = {"tiny": tiny, "attn": attn, "ffn": ffn, "batched": batched, "prefill": prefill}
 
 

@@ -165,3 +165,15 @@ def test_argmax_validation():
     assert _ma(work=BASE + 16) == ALIAS                           # workspace over W
     assert _ma(idx=BASE + 76 * MB + 16) == ALIAS                  # idx inside the workspace
     assert _ma(mode=3) == MODE
+
+
+@pytest.mark.parametrize("rows,n", [(1 << 40, 64), (1 << 62, 1), (64, 1 << 62), ((1 << 31) // 64 + 1, 64),
+                                    (3, (1 << 31) // 3 + 1)])
+def test_huge_sizes_are_rejected_before_any_product(rows, n):
+    """Sizes whose products would overflow int64 (or exceed the limits) are
+    refused by name, without forming rows * n first."""
+    assert _mm(rows=rows, n=n) == SHAPE
+    assert q8.lib().q8_block_sums(2, BASE, n, 256, rows, BASE + MB, BASE + 2 * MB, BASE + 3 * MB, None) == SHAPE
+    if n > (1 << 31):  # one row: only n can be too large
+        assert q8.lib().q8_matvec_argmax(1, BASE, n, 256, BASE + MB, None, BASE + 2 * MB, None, None,
+                                         BASE + 3 * MB, BASE + 4 * MB, BASE + 5 * MB, None) == SHAPE

@@ -48,3 +48,22 @@ def test_decode_layer_is_one_layers_projections():
     gate, up = calls[2], calls[3]
     assert gate.x_seed == up.x_seed and gate.w_seed != up.w_seed
     assert [c.residual_seed is not None for c in calls] == [False, True, False, False, True]
+
+
+def test_rows_summary_keys_on_the_metric_shapes():
+    """rows=1 is the 4096x14336 down projection alone (not mixed with the LM
+    head), rows=8 the two batched calls, rows=64 the prefill, and the LM head
+    is reported apart."""
+    wb = 62390272
+    per_call = {"down_i8x2": {"weight_bytes": wb, "project_us": 12.0},
+                "batch8": {"weight_bytes": wb, "project_us": 14.0},
+                "batch8_down_res": {"weight_bytes": wb, "project_us": 16.0},
+                "prefill64": {"weight_bytes": wb, "project_us": 34.0},
+                "lm_head": {"weight_bytes": 330612736, "project_us": 50.0}}
+    ceiling = {str(wb): {"us": 10.0}, "330612736": {"us": 48.0}}
+    s = bench.rows_summary(per_call, ceiling)
+    assert s["1"]["calls"] == ["down_i8x2"] and s["lm_head"]["calls"] == ["lm_head"]
+    assert abs(s["1"]["GBps"] - wb / 12.0 / 1e3) < 0.1
+    assert abs(s["8"]["GBps"] - 2 * wb / 30.0 / 1e3) < 0.1
+    assert s["64"]["pct_of_stream_ceiling"] == round(10.0 / 34.0 * 100, 1)
+    assert s["1"]["pct_hbm_peak"] == round(wb / 12.0 / 1e3 / 8000 * 100, 1)

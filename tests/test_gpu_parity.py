@@ -169,13 +169,36 @@ def test_matvec_entry_point():
 
 # ------------------------------------------------------------------ block sums
 
-@pytest.mark.parametrize("mode", ["i8", "i8x2"])
-@pytest.mark.parametrize("n,k,rows", [(256, 1024, 1), (4096, 4096, 1), (37, 2112, 3), (300, 4096, 8),
-                                      (64, 14336, 2)])
-def test_block_sums_bitwise(mode, n, k, rows):
+# q8_block_sums runs the kernel the projection of the same call dispatches to,
+# with its block-sum export on: the GEMV LDS ring (rows 1..2 and stacks the MFMA
+# kernels do not take), the one-thread-per-block stand-in for the GEMV kernels
+# without an export (k not a multiple of 256, or a stack staged in column
+# tiles), the wave-private MFMA kernel (one activation tile on short matrices)
+# and the shared-ring MFMA kernel in every (weight tiles, activation tiles)
+# class, two-word and one-word (one-word stacks of up to 8 rows in the
+# two-word layout), stacks over 64 rows (64-row slices), and the workload
+# shapes at full size.
+_SUMS_CASES = (
+    [(256, 1024, 1, m) for m in ("i8", "i8x2")]
+    + [(4096, 14336, 1, "i8x2"), (151936, 2048, 1, "i8"), (4096, 4096, 1, "i8x2")]   # GEMV ring, one row
+    + [(9000, 1024, 2, "i8x2"), (9000, 1024, 2, "i8")]                              # GEMV ring, two rows
+    + [(37, 2112, 3, "i8"), (13, 4160, 5, "i8x2"), (50, 4160, 8, "i8x2")]           # GEMV stand-in
+    + [(300, 4096, 8, "i8x2"), (4096, 14336, 8, "i8x2"), (1000, 2304, 7, "i8"),     # wave-private MFMA
+       (4000, 4096, 16, "i8"), (1, 256, 2, "i8x2"), (700, 2048, 2, "i8x2")]
+    + [(n, 1024, rows, mode) for n in (2000, 6000, 9000)                              # shared-ring MFMA
+       for rows, mode in ((5, "i8"), (24, "i8"), (64, "i8"), (5, "i8x2"), (12, "i8x2"), (24, "i8x2"),
+                          (64, "i8x2"))]
+    + [(14336, 4096, 8, "i8x2"), (14336, 4096, 64, "i8"), (14336, 4096, 2, "i8x2")]  # workload shapes
+    + [(515, 4096, r, m) for r in (3, 9, 17, 33, 63) for m in ("i8", "i8x2")]        # ragged stacks
+    + [(100, 512, 70, "i8x2"), (333, 768, 129, "i8")]                                 # over 64 rows
+)
+
+
+@pytest.mark.parametrize("n,k,rows,mode", _SUMS_CASES, ids=lambda v: str(v))
+def test_block_sums_bitwise(n, k, rows, mode):
     say("block_sums", mode, n, k, rows)
-    w = synth.weights(n, k, seed=90 + rows, outlier_frac=0.01)
-    x = synth.activations(rows, k, seed=95 + rows, outlier_frac=0.005)
+    w = synth.weights(n, k, seed=90 + rows + n % 7, outlier_frac=0.01)
+    x = synth.activations(rows, k, seed=95 + rows + k % 5, outlier_frac=0.005)
     blocks = oracle.quantize_weights(w)
     hi, lo, sc = oracle.quantize_act(mode, x)
     got = q8.block_sums(mode, to_dev(blocks), n, k, to_dev(hi), None if lo is None else to_dev(lo))
@@ -323,6 +346,7 @@ def test_argmax_fused_into_the_projection(n, k, mode, with_res, inside):
         ohi, olo, osc = oracle.quantize_act(mode, x[None])
         r, a = oracle.project(mode, oracle.quantize_weights(w), n, k, 1, hi=ohi, lo=olo, scale=osc,
                               residual=None if res is None else res[None])
+    gate(y_ref.cpu().numpy()[None], r, a, f"argmax head y {n}x{k} {mode}")
     r, a = r[0], a[0]
     top = np.argsort(r)[::-1][:2]
     tol = 1e-5 * abs(r[top]) + 2.0 ** -40 * a[top]

@@ -329,3 +329,50 @@ def test_modes_agree_to_their_precision():
         qa = np.abs(q).reshape(32, -1, 32).sum(axis=2)
         bound = (scales.view(np.float16).astype(np.float64) * qa) @ s[0].astype(np.float64) * (step + 2.0 ** -15)
         assert (np.abs(y[0] - y0[0]) <= bound + 1e-12 * a0[0]).all()
+
+
+def _error_scale_numpy(mode, blocks, n, k, x, residual):
+    """A = sum_b |block term| + |residual|, written independently of the oracle:
+    the block sums from numpy's int64 einsum (integer modes) or f64 einsum (f32
+    mode), every block term formed in f64 from the block's binary16 and f32
+    scales as numpy decodes them."""
+    scales, q = oracle.split_blocks(blocks, n, k)
+    d = scales.view(np.float16).astype(np.float64)                    # [n][nb]
+    qb = q.reshape(n, k // 32, 32)
+    if mode == "f32":
+        xb = x.astype(np.float64).reshape(x.shape[0], k // 32, 32)
+        terms = d[None] * np.einsum("nbj,rbj->rnb", qb.astype(np.float64), xb)
+    else:
+        hi, lo, s = oracle.quantize_act(mode, x)
+        rows = x.shape[0]
+        sh = np.einsum("nbj,rbj->rnb", qb.astype(np.int64), hi.reshape(rows, k // 32, 32).astype(np.int64))
+        t = sh.astype(np.float64)
+        if mode == "i8x2":
+            sl = np.einsum("nbj,rbj->rnb", qb.astype(np.int64), lo.reshape(rows, k // 32, 32).astype(np.int64))
+            t = t + sl.astype(np.float64) / 128.0
+        terms = d[None] * s.astype(np.float64)[:, None, :] * t
+    a = np.abs(terms).sum(axis=2)
+    if residual is not None:
+        a = a + np.abs(residual.astype(np.float64))
+    return a
+
+
+@pytest.mark.parametrize("mode", ["f32", "i8", "i8x2"])
+@pytest.mark.parametrize("n,k,rows,seed,with_res", [(17, 128, 3, 31, True), (40, 1024, 2, 32, False),
+                                                    (9, 4096, 1, 33, True)])
+def test_error_scale_pinned_from_both_sides(mode, n, k, rows, seed, with_res):
+    """The oracle's error scale A (which sets the floor of every parity gate)
+    equals an independent numpy computation of sum_b |block term| + |residual|
+    up to summation order (relative 1e-12), so it can be neither inflated nor
+    shrunk without failing here."""
+    w = synth.weights(n, k, seed=seed, outlier_frac=0.1)
+    x = synth.activations(rows, k, seed=seed + 1, outlier_frac=0.05)
+    res = synth.normal(seed + 2, (rows, n)) if with_res else None
+    blocks = oracle.quantize_weights(w)
+    if mode == "f32":
+        _, a = oracle.project(mode, blocks, n, k, rows, x=x, residual=res)
+    else:
+        hi, lo, s = oracle.quantize_act(mode, x)
+        _, a = oracle.project(mode, blocks, n, k, rows, hi=hi, lo=lo, scale=s, residual=res)
+    ref = _error_scale_numpy(mode, blocks, n, k, x, res)
+    assert np.allclose(a, ref, rtol=1e-12, atol=0.0), float(np.max(np.abs(a / ref - 1)))

@@ -15,7 +15,7 @@ import pytest
 import oracle
 import synth
 
-from test_oracle import block_from, read_golden
+from test_oracle import _error_scale_numpy, block_from, read_golden
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "q8ref.c")
 
@@ -34,6 +34,9 @@ MUTANTS = {
     "f16_truncates": ("double m = rint(a / quantum);", "double m = floor(a / quantum);"),
     "residual_dropped": ("        y += res;\n", "        (void)res;\n"),
     "f32_mode_weight_scale_dropped": ("            term = d * p;", "            term = p;"),
+    "error_scale_doubled": ("        a += fabs(term);\n", "        a += 2.0 * fabs(term);\n"),
+    "error_scale_signed": ("        a += fabs(term);\n", "        a += term;\n"),
+    "error_scale_residual_twice": ("        a += fabs(res);\n", "        a += 2.0 * fabs(res);\n"),
     "amax_signed": ("if (fabsf(src[j]) > amax) amax = fabsf(src[j]);\n            float s",
                     "if (src[j] > amax) amax = src[j];\n            float s"),
 }
@@ -89,6 +92,14 @@ def _pins():
         check(f"act bound {mode}", (err <= se * (step + 2.0 ** -16)).all())
     y, a = oracle.project("f32", b, n, k, rows, x=x)
     check("brute f32", (np.abs(y - x.astype(np.float64) @ wd.T) <= 1e-12 * a).all())
+    res = synth.normal(63, (rows, n))
+    for mode in ("f32", "i8", "i8x2"):
+        if mode == "f32":
+            _, a = oracle.project(mode, b, n, k, rows, x=x, residual=res)
+        else:
+            hi, lo, s = oracle.quantize_act(mode, x)
+            _, a = oracle.project(mode, b, n, k, rows, hi=hi, lo=lo, scale=s, residual=res)
+        check(f"error scale {mode}", np.allclose(a, _error_scale_numpy(mode, b, n, k, x, res), rtol=1e-12, atol=0.0))
     return failures
 
 
