@@ -169,6 +169,24 @@ q8_status q8_matvec_argmax(int mode, const void *w, int64_t n, int64_t k, const 
  * device (0 if n is out of range). */
 int64_t q8_argmax_workspace_bytes(int64_t n);
 
+/* q8_matvec_argmax for callers that cannot allocate: code under HIP graph
+ * capture, serving loops that may not call hipMalloc, harnesses that forbid
+ * it.  Arguments, results and limits as q8_matvec_argmax, without the
+ * workspace: the library uses a fixed 64 KiB device array of its own instead
+ * (one per GPU, held until the process ends; its address is looked up once per
+ * device, on the first call there).  Each call clears the array's counter with
+ * a one-workgroup kernel on `stream`, then launches the projection; nothing is
+ * allocated, freed or set with a memset, so the pair can be captured into a
+ * graph.  Every call on one GPU shares that GPU's array: calls that overlap on
+ * one GPU (other streams, other threads) race, and the caller must serialize
+ * them.  Limit: q8_argmax_workspace_bytes(n) <= 65536 (n up to about 4.19
+ * million rows on a 256-CU device), else Q8_E_SHAPE.
+ * Errors: as q8_matvec_argmax; Q8_E_HIP also if the array's address cannot be
+ * found. */
+q8_status q8_matvec_argmax_noalloc(int mode, const void *w, int64_t n, int64_t k, const int8_t *hi,
+                                   const int8_t *lo, const float *scale, const float *x, const float *residual,
+                                   float *y, int32_t *idx, void *stream);
+
 /* The exact int32 block dot products of the integer modes, for checking:
  *   sums[r][n][b][0] = sum_j q[n][b][j] * hi[r][32b+j]
  *   sums[r][n][b][1] = sum_j q[n][b][j] * lo[r][32b+j]   (Q8_ACT_I8X2 only)

@@ -38,6 +38,7 @@ SIGNATURES = {
     "q8_matmul_rows": (_I, [_I, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "q8_matvec_argmax": (_I, [_I, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "q8_argmax_workspace_bytes": (_I64, [_I64]),
+    "q8_matvec_argmax_noalloc": (_I, [_I, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
     "q8_block_sums": (_I, [_I, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "q8_status_name": (ctypes.c_char_p, [_I]),
     "q8_version": (_I, []),
@@ -235,6 +236,28 @@ def matvec_argmax(mode, w: torch.Tensor, n: int, k: int, hi=None, lo=None, scale
     _check("q8_matvec_argmax", lib().q8_matvec_argmax(m, _ptr(w), n, k, _ptr(hi), _ptr(lo), _ptr(scale), _ptr(x),
                                                       _ptr(residual), _ptr(out), _ptr(idx), _ptr(workspace),
                                                       _stream(stream)))
+    return out, idx
+
+
+def matvec_argmax_noalloc(mode, w: torch.Tensor, n: int, k: int, hi=None, lo=None, scale=None, x=None,
+                          residual=None, out=None, idx=None, stream=None):
+    """matvec_argmax with the library's own fixed workspace (q8_matvec_argmax_noalloc):
+    the call itself allocates nothing when out and idx are given.  Calls that
+    overlap on one GPU race."""
+    m = _mode(mode)
+    dev = _device_of(w, hi, x)
+    if out is None:
+        out = torch.empty((n,), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((1,), dtype=torch.int32, device=dev)
+    _want_weights(w, n, k)
+    _want_stack(m, 1, k, hi, lo, scale, x)
+    _want(residual, "residual", torch.float32, n, optional=True)
+    _want(out, "out", torch.float32, n)
+    _want(idx, "idx", torch.int32, 1)
+    _check("q8_matvec_argmax_noalloc",
+           lib().q8_matvec_argmax_noalloc(m, _ptr(w), n, k, _ptr(hi), _ptr(lo), _ptr(scale), _ptr(x),
+                                          _ptr(residual), _ptr(out), _ptr(idx), _stream(stream)))
     return out, idx
 
 

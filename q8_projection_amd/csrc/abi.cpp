@@ -202,9 +202,16 @@ int64_t q8_argmax_workspace_bytes(int64_t n) {
     return 16 + 8 * q8::gemv_row_grid(n);
 }
 
-q8_status q8_matvec_argmax(int mode, const void *w, int64_t n, int64_t k, const int8_t *hi, const int8_t *lo,
-                           const float *scale, const float *x, const float *residual, float *y, int32_t *idx,
-                           void *workspace, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by the two fused arg-max entry points.  The
+// workspace is the caller's (checked for alignment and overlap) or the
+// library's own array (owned = false: it overlaps nothing of the caller's).
+q8_status argmax_projection(int mode, const void *w, int64_t n, int64_t k, const int8_t *hi, const int8_t *lo,
+                            const float *scale, const float *x, const float *residual, float *y, int32_t *idx,
+                            void *workspace, bool caller_workspace, void *stream) {
     if (q8_status s = check_sizes(n, k, 1); s != Q8_OK) return s;  // before n * 4 is formed
     if (q8_status s = check_projection(mode, w, n, k, 1, hi, lo, scale, x, residual, y, n * 4, true, true);
         s != Q8_OK)
@@ -212,9 +219,9 @@ q8_status q8_matvec_argmax(int mode, const void *w, int64_t n, int64_t k, const 
     if (n < 1 || n > INT32_MAX) return Q8_E_SHAPE;
     // one launch: the weights in one buffer and the stack resident in LDS
     if (n * (k / 32) * 34 > (int64_t(1) << 30) || !q8::gemv_row_resident(mode, k)) return Q8_E_SHAPE;
-    if (!idx || !workspace) return Q8_E_NULL;
-    if (!aligned(idx, 4) || !aligned(workspace, 16)) return Q8_E_ALIGN;
-    const int64_t wsb = q8_argmax_workspace_bytes(n);
+    if (!idx || (caller_workspace && !workspace)) return Q8_E_NULL;
+    if (!aligned(idx, 4) || (caller_workspace && !aligned(workspace, 16))) return Q8_E_ALIGN;
+    const int64_t wsb = caller_workspace ? q8_argmax_workspace_bytes(n) : 0;
     const int64_t wbytes = n * (k / 32) * 34;
     const bool inside = mode != Q8_ACT_F32 && !hi;
     const void *ins[] = {w, hi, lo, scale, x, residual, y};
@@ -225,6 +232,13 @@ q8_status q8_matvec_argmax(int mode, const void *w, int64_t n, int64_t k, const 
         if (ins[i] && in_bytes[i] > 0 && (overlap(idx, 4, ins[i], in_bytes[i]) || overlap(workspace, wsb, ins[i], in_bytes[i])))
             return Q8_E_ALIAS;
     if (overlap(idx, 4, workspace, wsb)) return Q8_E_ALIAS;
+    if (!caller_workspace) {
+        // the library's array: at most its size, found once per device, its
+        // counter cleared on this stream before the projection
+        if (q8_argmax_workspace_bytes(n) > q8::argmax_scratch_bytes()) return Q8_E_SHAPE;
+        if (q8::argmax_scratch(&workspace) != hipSuccess) return Q8_E_HIP;
+        if (q8::launch_clear_argmax_header(workspace, as_stream(stream)) != hipSuccess) return Q8_E_HIP;
+    }
     const hipError_t e = q8::launch_gemv(mode, static_cast<const uint8_t *>(w), n, k, 1,
                                          (mode == Q8_ACT_F32 || inside) ? nullptr : hi,
                                          (mode == Q8_ACT_I8X2 && !inside) ? lo : nullptr,
@@ -232,6 +246,22 @@ q8_status q8_matvec_argmax(int mode, const void *w, int64_t n, int64_t k, const 
                                          (mode == Q8_ACT_F32 || inside) ? x : nullptr, residual, y, as_stream(stream),
                                          idx, workspace);
     return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+q8_status q8_matvec_argmax(int mode, const void *w, int64_t n, int64_t k, const int8_t *hi, const int8_t *lo,
+                           const float *scale, const float *x, const float *residual, float *y, int32_t *idx,
+                           void *workspace, void *stream) {
+    return argmax_projection(mode, w, n, k, hi, lo, scale, x, residual, y, idx, workspace, true, stream);
+}
+
+q8_status q8_matvec_argmax_noalloc(int mode, const void *w, int64_t n, int64_t k, const int8_t *hi,
+                                   const int8_t *lo, const float *scale, const float *x, const float *residual,
+                                   float *y, int32_t *idx, void *stream) {
+    return argmax_projection(mode, w, n, k, hi, lo, scale, x, residual, y, idx, nullptr, false, stream);
 }
 
 q8_status q8_block_sums(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,

@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["q8_quantize_weights", "q8_quantize_act", "q8_matvec", "q8_matmul_rows",
-                            "q8_matvec_argmax", "q8_argmax_workspace_bytes", "q8_block_sums",
+                            "q8_matvec_argmax", "q8_argmax_workspace_bytes", "q8_matvec_argmax_noalloc",
+                            "q8_block_sums",
                             "q8_status_name", "q8_version"])
 
 
@@ -177,3 +178,23 @@ def test_huge_sizes_are_rejected_before_any_product(rows, n):
     if n > (1 << 31):  # one row: only n can be too large
         assert q8.lib().q8_matvec_argmax(1, BASE, n, 256, BASE + MB, None, BASE + 2 * MB, None, None,
                                          BASE + 3 * MB, BASE + 4 * MB, BASE + 5 * MB, None) == SHAPE
+
+
+def test_noalloc_argmax_refuses_what_its_array_cannot_hold():
+    """q8_matvec_argmax_noalloc checks its arguments as q8_matvec_argmax does,
+    and refuses a head whose partials would not fit its fixed 64 KiB array
+    (every call here fails a check before anything is looked up or launched)."""
+    f = q8.lib().q8_matvec_argmax_noalloc
+    big = 5_000_000                       # 4.19 M rows is the most the array holds
+    assert q8.lib().q8_argmax_workspace_bytes(big) > 65536
+    assert f(1, BASE, big, 64, BASE + 512 * MB, None, BASE + 600 * MB, None, None, BASE + 700 * MB,
+             BASE + 800 * MB, None) == SHAPE
+    assert f(1, BASE, 64, 256, BASE + MB, None, BASE + 2 * MB, None, None, BASE + 3 * MB, None, None) == NULL
+    assert f(1, BASE, 64, 256, BASE + MB, None, BASE + 2 * MB, None, None, BASE + 3 * MB, BASE + 4 * MB + 2,
+             None) == ALIGN
+    assert f(0, BASE, 64, 256, None, None, None, None, None, BASE + 3 * MB, BASE + 4 * MB, None) == NULL
+    assert f(1, BASE, 64, 96, BASE + MB, None, BASE + 2 * MB, None, None, BASE + 3 * MB, BASE + 4 * MB,
+             None) == SHAPE
+    # idx inside y
+    assert f(1, BASE, 64, 256, BASE + MB, None, BASE + 2 * MB, None, None, BASE + 3 * MB, BASE + 3 * MB + 8,
+             None) == ALIAS
