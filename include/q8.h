@@ -190,9 +190,11 @@ q8_status q8_matvec_argmax_noalloc(int mode, const void *w, int64_t n, int64_t k
 /* The exact int32 block dot products of the integer modes, for checking:
  *   sums[r][n][b][0] = sum_j q[n][b][j] * hi[r][32b+j]
  *   sums[r][n][b][1] = sum_j q[n][b][j] * lo[r][32b+j]   (Q8_ACT_I8X2 only)
- * computed with the same device block decode and dot routine as the GEMV
- * projection kernels (the MFMA kernels' int32 sums are checked through their
- * outputs).  sums: out, int32 [rows][n][k/32][words],
+ * computed by the kernel that q8_matmul_rows runs for the same stack (the
+ * same 64-row slices and 8-row GEMV chunks, the GEMV or MFMA kernel and its
+ * wave split, with the scales counted as 16-byte aligned), with that kernel's
+ * block-sum export on: it writes each block's int32 sums where the projection
+ * scales and accumulates them.  sums: out, int32 [rows][n][k/32][words],
  * 4-byte aligned.  Errors as q8_matmul_rows (Q8_ACT_F32: Q8_E_MODE). */
 q8_status q8_block_sums(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
                         const int8_t *lo, int32_t *sums, void *stream);

@@ -160,14 +160,16 @@ __device__ __forceinline__ void staged_barrier() {
 }
 
 // Integer modes.  LDS: hi [R][kt] bytes, lo [R][kt] bytes (two-word), scales [R][kt/32] f32.
-template <int R, int WORDS>
+// SUMS: the block-sum export has no scales; they are not copied.
+template <int R, int WORDS, bool SUMS = false>
 __device__ __forceinline__ void stage_int(const GemvArgs &a, uint8_t *lds, int ti, int wave, int lane) {
     const int kt0 = ti * a.kt, ktc = min(a.kt, a.k - kt0);
     dma_rows16(lds, a.kt, reinterpret_cast<const uint8_t *>(a.hi) + kt0, a.k, R, ktc, wave, lane);
     if (WORDS == 2)
         dma_rows16(lds + R * a.kt, a.kt, reinterpret_cast<const uint8_t *>(a.lo) + kt0, a.k, R, ktc, wave, lane);
-    dma_rows4(reinterpret_cast<float *>(lds + WORDS * R * a.kt), a.kt / kBlock, a.scale + kt0 / kBlock, a.nb, R,
-              ktc / kBlock, wave, lane);
+    if constexpr (!SUMS)
+        dma_rows4(reinterpret_cast<float *>(lds + WORDS * R * a.kt), a.kt / kBlock, a.scale + kt0 / kBlock, a.nb,
+                  R, ktc / kBlock, wave, lane);
 }
 
 // Integer modes with the stack given as f32 x: each workgroup quantizes the
@@ -346,10 +348,12 @@ __device__ __forceinline__ void compute_item(const GemvArgs &a, const uint8_t *l
         compute_int_item<R, WORDS, MR, SUMS>(a, lds, it, lane, win, acc);
 }
 
-template <int R, int WORDS>
+template <int R, int WORDS, bool SUMS = false>
 __device__ __forceinline__ void stage_tile(const GemvArgs &a, uint8_t *lds, int ti, int wave, int lane) {
     if constexpr (WORDS == 0)
         stage_f32<R>(a, lds, ti, wave, lane);
+    else if constexpr (SUMS)
+        stage_int<R, WORDS, true>(a, lds, ti, wave, lane);
     else if (a.x)
         stage_quant<R, WORDS>(a, lds, ti);
     else
@@ -528,8 +532,10 @@ struct Cursor {
     }
 };
 
-// WORDS = 1 or 2 (integer modes) or 0 (f32 mode).
-template <int R, int WORDS, int MR, int P>
+// WORDS = 1 or 2 (integer modes) or 0 (f32 mode).  SUMS: export the block
+// sums instead of writing y (every memory operation of the loop is the
+// compiler's, so it orders the export's stores itself).
+template <int R, int WORDS, int MR, int P, bool SUMS = false>
 __global__ __launch_bounds__(kThreads) void gemv_resident_kernel(GemvArgs a) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & 63;
@@ -560,7 +566,7 @@ __global__ __launch_bounds__(kThreads) void gemv_resident_kernel(GemvArgs a) {
 
     // Prologue: stage the stack (L2), then put the first P items of weights (HBM)
     // in flight, and barrier once the stack has landed.
-    stage_tile<R, WORDS>(a, lds, 0, wave, lane);
+    stage_tile<R, WORDS, SUMS>(a, lds, 0, wave, lane);
     Window ring[P][MR];
     Cursor ahead{0, 0};
 #pragma unroll
@@ -581,7 +587,7 @@ __global__ __launch_bounds__(kThreads) void gemv_resident_kernel(GemvArgs a) {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const Item it{gw + static_cast<int64_t>(cur.gi) * stride, 0, cur.u};
-            compute_item<R, WORDS, MR>(a, lds, it, lane, ring[p], acc);
+            compute_item<R, WORDS, MR, SUMS>(a, lds, it, lane, ring[p], acc);
             stream_item<MR>(ws, item_base(ahead), lane_ok(ahead), ring[p]);
             ahead.next(ub);
             if (cur.gi < G && cur.u == ub - 1) {
@@ -597,6 +603,7 @@ __global__ __launch_bounds__(kThreads) void gemv_resident_kernel(GemvArgs a) {
             cur.next(ub);
         }
     }
+    if constexpr (SUMS) return;
     wave_lds_sync();  // lane 0 parked the totals the whole wave reads now
     finish_rows<R, WORDS, MR>(a, totals, G, gw, stride, wave, lane);
 }
@@ -895,7 +902,9 @@ __global__ __launch_bounds__(kThreads) void gemv_ring_kernel(GemvArgs a) {
 
 // The stack is staged one column tile at a time; each wave owns one row group and
 // keeps its (at most kTiledMaxUb) items of the tile in registers.
-template <int R, int WORDS, int MR>
+// SUMS: export the block sums instead of writing y; the export's stores are
+// waited for before the next tile's copies are counted.
+template <int R, int WORDS, int MR, bool SUMS = false>
 __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(GemvArgs a) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & 63;
@@ -908,7 +917,7 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(GemvArgs a) {
         for (int r = 0; r < R; ++r) acc[m][r] = 0.0;
     for (int ti = 0; ti < a.ntiles; ++ti) {
         if (ti > 0) __syncthreads();  // every wave is done with the previous tile
-        stage_tile<R, WORDS>(a, lds, ti, wave, lane);
+        stage_tile<R, WORDS, SUMS>(a, lds, ti, wave, lane);
         Window win[kTiledMaxUb][MR];
 #pragma unroll
         for (int u = 0; u < kTiledMaxUb; ++u)
@@ -916,8 +925,10 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(GemvArgs a) {
         staged_barrier<kTiledMaxUb * MR * kLoadsPerWindow>();
 #pragma unroll
         for (int u = 0; u < kTiledMaxUb; ++u)
-            if (u < a.ub) compute_item<R, WORDS, MR>(a, lds, Item{grp, ti, u}, lane, win[u], acc);
+            if (u < a.ub) compute_item<R, WORDS, MR, SUMS>(a, lds, Item{grp, ti, u}, lane, win[u], acc);
+        if constexpr (SUMS) wait_vm<0>();
     }
+    if constexpr (SUMS) return;
     const double post = WORDS == 2 ? 1.0 / 128.0 : 1.0;
 #pragma unroll
     for (int m = 0; m < MR; ++m)
@@ -961,16 +972,9 @@ bool ring_serves(const GemvArgs &a) {
            ring_lds_bytes<R, WORDS, MR, P>(a.k) * 2 <= static_cast<size_t>(device_info().lds_per_block);
 }
 
-// SUMS: the block-sum export of the same call.  Where the ring kernel serves
-// it, that kernel exports; the other kernels (unaligned or tiled stacks) are
-// stood in for by block_sums_kernel, which decodes and multiplies each block
-// as they do.
+// SUMS: the block-sum export of the same call, from the kernel that projects it.
 template <int R, int WORDS, int MR, int P, bool SUMS = false>
 hipError_t run(GemvArgs a, hipStream_t stream) {
-    if constexpr (SUMS) {
-        if (!ring_serves<R, WORDS, MR, P>(a))
-            return launch_block_sums(WORDS, a.w, a.n, a.k, R, a.hi, a.lo, a.sums, a.sums_ld, stream);
-    }
     a.kt = tile_columns(a.k, R, WORDS);
     a.ntiles = (a.k + a.kt - 1) / a.kt;
     a.ub = (a.kt / kBlock + 63) / 64;
@@ -1023,12 +1027,12 @@ hipError_t run(GemvArgs a, hipStream_t stream) {
                 gemv_ring_kernel<R, WORDS, MR, P, false><<<g, kThreads, ring_lds, stream>>>(b);
             else
                 gemv_ring_kernel<R, WORDS, MR, P, true><<<g, kThreads, ring_lds, stream>>>(b);
-        } else if constexpr (!SUMS) {
-            gemv_resident_kernel<R, WORDS, MR, P><<<dim3(static_cast<unsigned>(grid)), kThreads, lds, stream>>>(a);
+        } else {
+            gemv_resident_kernel<R, WORDS, MR, P, SUMS><<<dim3(static_cast<unsigned>(grid)), kThreads, lds, stream>>>(a);
         }
-    } else if constexpr (!SUMS) {
+    } else {
         const int64_t grid = (a.num_groups + kWaves - 1) / kWaves;
-        gemv_tiled_kernel<R, WORDS, MR><<<dim3(static_cast<unsigned>(grid)), kThreads, stack, stream>>>(a);
+        gemv_tiled_kernel<R, WORDS, MR, SUMS><<<dim3(static_cast<unsigned>(grid)), kThreads, stack, stream>>>(a);
     }
     return hipGetLastError();
 }

@@ -57,8 +57,6 @@ hipError_t launch_mma_sums(int mode, const uint8_t *w, int64_t n, int64_t k, int
 bool mma_supports(int mode, int64_t n, int64_t k, int rows, const void *w, const void *hi, const void *lo,
                   const void *scale);
 
-// One thread per weight block: the block sums as the resident and tiled GEMV
-// kernels form them (sums row stride sums_ld weight rows).
 // The fixed device array that stands in for the fused arg-max's workspace in
 // q8_matvec_argmax_noalloc: its size, its address on the current device
 // (looked up once per device), and a kernel that clears its counter.
@@ -66,8 +64,5 @@ int64_t argmax_scratch_bytes();
 hipError_t argmax_scratch(void **out);
 hipError_t launch_clear_argmax_header(void *workspace, hipStream_t stream);
 
-hipError_t launch_block_sums(int words, const uint8_t *w, int64_t n, int64_t k, int64_t rows,
-                             const int8_t *hi, const int8_t *lo, int32_t *sums, int64_t sums_ld,
-                             hipStream_t stream);
 
 }  // namespace q8
