@@ -145,33 +145,64 @@ class Prepared:
                            residual=self.res, out=self.y)
 
 
-def sweep(spec: str, dev):
+def sweep(spec: str, dev, only_rows: int | None = None, launches: int = 0):
     """Kernel time of one projection per stack height (rows 1..64) through the
     library's own dispatch: "N,K,MODE", e.g. "14336,4096,i8x2".  Prints one JSON
-    line per height."""
+    line per height.  With `only_rows`: run that height alone, eagerly,
+    `launches` times (for profilers), and print one line."""
     import dataclasses
     import torch
+    import q8_projection_amd as q8
     from synth import workloads as wl
     n, k, mode = spec.split(",")
     base = wl.Call(f"sweep_{n}x{k}_{mode}", int(n), int(k), 64, mode, "matmul_rows", w_seed=900, x_seed=901)
     p = Prepared(base, dev)
     p.quantize()
-    for rows in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64):
-        call = dataclasses.replace(base, rows=rows)
 
-        def launch(i, rows=rows):
-            import q8_projection_amd as q8
+    def launch(i, rows):
+        if mode == "f32":
+            q8.matmul_rows(mode, p.w[i % p.copies], base.n, base.k, x=p.x[:rows], out=p.y[:rows])
+        else:
             lo = None if p.lo is None else p.lo[:rows]
-            q8.matmul_rows(mode, p.w[i % p.copies], call.n, call.k, hi=p.hi[:rows], lo=lo, scale=p.sc[:rows],
+            q8.matmul_rows(mode, p.w[i % p.copies], base.n, base.k, hi=p.hi[:rows], lo=lo, scale=p.sc[:rows],
                            out=p.y[:rows])
 
+    if only_rows is not None:
+        if not 1 <= only_rows <= 64:
+            raise ValueError("--rows: 1..64")
+        torch.cuda.synchronize()
+        for i in range(launches):
+            launch(i, only_rows)
+        torch.cuda.synchronize()
+        call = dataclasses.replace(base, rows=only_rows)
+        print(json.dumps({"sweep": f"{n}x{k}", "mode": mode, "rows": only_rows, "launches": launches,
+                          "weight_bytes_per_launch": call.weight_bytes}), flush=True)
+        return
+    for rows in (1, 2, 3, 4, 6, 8, 9, 12, 16, 24, 32, 48, 64):
+        call = dataclasses.replace(base, rows=rows)
         reps = 20
-        g = capture(lambda: [launch(i) for i in range(reps)])
+        g = capture(lambda rows=rows: [launch(i, rows) for i in range(reps)])
         t = time_graph(g, 5) / reps
         print(json.dumps({"sweep": f"{n}x{k}", "mode": mode, "rows": rows, "project_us": round(t * 1e6, 3),
                           "GBps": round(call.weight_bytes / t / 1e9, 1),
                           "pct_hbm_peak": round(call.weight_bytes / t / 1e9 / HBM_PEAK_GBPS * 100, 1),
                           "rows_GFLOPs": round(call.flops / t / 1e9, 1)}), flush=True)
+
+
+def calib_copies(mib: int, dev) -> int:
+    """torch's device copy of `mib` MiB, four times: the known-size reference
+    that HBM byte counters are scaled by.  Returns the bytes of one copy."""
+    import torch
+    if not mib:
+        return 0
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return n
 
 
 def time_calls(prepared, reps):
@@ -479,8 +510,10 @@ def main(argv=None):
     ap.add_argument("--only", default=None, help="run only the named call eagerly (for profilers)")
     ap.add_argument("--sweep", default=None, metavar="N,K,MODE",
                     help="time one projection shape at stack heights 1..64 instead of the step")
+    ap.add_argument("--rows", type=int, default=None,
+                    help="with --sweep: run only this stack height, eagerly, warmup + steps launches (for profilers)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="with --only: also run torch's device copy of this many MiB, 4 times (the "
+                    help="with --only or --sweep --rows: also run torch's device copy of this many MiB, 4 times (the "
                          "known-size reference for HBM byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -496,7 +529,9 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.sweep:
-        sweep(args.sweep, dev)
+        sweep(args.sweep, dev, args.rows, args.warmup + args.steps)
+        if args.rows is not None and args.calib_copy_mib:
+            print(json.dumps({"calib_copy_bytes_each": calib_copies(args.calib_copy_mib, dev)}))
         return 0
     if args.only:
         from synth import workloads as wl
@@ -510,18 +545,9 @@ def main(argv=None):
         for i in range(args.warmup + args.steps):
             p.project(i % p.copies)
         torch.cuda.synchronize()
-        copied = 0
-        if args.calib_copy_mib:
-            n = args.calib_copy_mib << 20
-            src = torch.ones(n, dtype=torch.uint8, device=dev)
-            dst = torch.empty_like(src)
-            torch.cuda.synchronize()
-            for _ in range(4):
-                dst.copy_(src)
-                copied += n
-            torch.cuda.synchronize()
+        copied = calib_copies(args.calib_copy_mib, dev)
         print(json.dumps({"only": args.only, "launches": args.warmup + args.steps,
-                          "weight_bytes_per_launch": p.call.weight_bytes, "calib_copy_bytes_each": copied // 4}))
+                          "weight_bytes_per_launch": p.call.weight_bytes, "calib_copy_bytes_each": copied}))
         return 0
 
     calls = step_calls()

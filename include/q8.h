@@ -134,9 +134,14 @@ q8_status q8_matvec(int mode, const void *w, int64_t n, int64_t k, const int8_t 
  * prefill; codegen_cuda::lane page, description: chunks of 2, 4, ... rows).
  * Arguments as q8_matvec with [rows][...] stacks: hi/lo/x [rows][k],
  * scale [rows][k/32], residual and y [rows][n].  rows >= 1; stacks wider than
- * 64 rows are run as consecutive 64-row slices.  An integer-mode stack given
- * as x (hi, lo, scale NULL) is quantized inside the projection as in
- * q8_matvec; such calls run on the GEMV kernels, eight rows at a time.
+ * 64 rows are run as consecutive 64-row slices.  Kernels: integer stacks of
+ * 2..64 rows on int8 MFMA tiles (or the GEMV for short stacks), f32 stacks of
+ * 5..64 rows on f64 MFMA tiles (sums still exact products added in f64), up to
+ * 4 rows on the GEMV; each slice streams the weights once.  An integer-mode
+ * stack given as x (hi, lo, scale NULL) is quantized inside the projection as
+ * in q8_matvec, for at most 8 rows (one GEMV pass); a taller one is
+ * Q8_E_SHAPE: quantize it once with q8_quantize_act (the result serves every
+ * projection of the same input) and pass hi, lo and scale.
  * Errors: Q8_E_NULL, Q8_E_SHAPE, Q8_E_ALIGN, Q8_E_MODE, Q8_E_ALIAS, Q8_E_HIP. */
 q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
                          const int8_t *lo, const float *scale, const float *x, const float *residual,

@@ -177,7 +177,8 @@ def quantize_act(mode, x: torch.Tensor, hi=None, lo=None, scale=None, stream=Non
 def matmul_rows(mode, w: torch.Tensor, n: int, k: int, hi=None, lo=None, scale=None, x=None,
                 residual=None, out=None, rows: int | None = None, stream=None) -> torch.Tensor:
     """Y [rows][n] = X W^T (+ residual) over a stack of activation rows.  In an
-    integer mode, x alone (hi, lo, scale None) is quantized inside the call."""
+    integer mode, x alone (hi, lo, scale None) is quantized inside the call, for
+    stacks of at most 8 rows."""
     m = _mode(mode)
     src = x if (m == 0 or hi is None) else hi
     if rows is None:

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libq8proj.so")
 PROBE_LIB = os.path.join(HERE, "libq8probe.so")
 PROBE_SOURCES = ["stream_probe.hip"]
 SOURCES = ["abi.cpp", "quantize.hip", "gemv.hip", "gemv_f32.hip", "gemv_i8.hip", "gemv_i8x2.hip",
-           "gemv_sums.hip", "mma.hip", "mma_sums.hip", "argmax_noalloc.hip"]
+           "gemv_sums.hip", "mma.hip", "mma_sums.hip", "f64mma.hip", "argmax_noalloc.hip"]
 ARCH = "gfx950"
 
 # Packed f32 VALU ops are kept out of the device code; the host pass warns that

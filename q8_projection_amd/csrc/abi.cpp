@@ -17,6 +17,7 @@ namespace {
 constexpr int64_t kMaxK = int64_t(1) << 24;           // columns
 constexpr int64_t kMaxBlocks = int64_t(1) << 27;      // n * k/32 (4.5 GB of weights)
 constexpr int64_t kMaxRowsTimesN = int64_t(1) << 31;  // elements of y
+constexpr int64_t kMaxInsideRows = 8;                 // integer stacks quantized inside a projection
 constexpr int kMaxDevices = 64;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -160,6 +161,9 @@ q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t 
     if (q8_status s = check_projection(mode, w, n, k, rows, hi, lo, scale, x, residual, y, rows * n * 4, true, true);
         s != Q8_OK)
         return s;
+    // An integer-mode stack given as x is quantized inside the GEMV, which
+    // takes at most 8 rows in one pass over the weights.
+    if (mode != Q8_ACT_F32 && !hi && rows > kMaxInsideRows) return Q8_E_SHAPE;
     if (n == 0 || rows == 0) return Q8_OK;
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const int64_t nb = k / 32;
@@ -177,6 +181,8 @@ q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t 
         hipError_t e;
         if (mma_serves(mode, n, k, r, wb, shi, slo, ssc, inside)) {
             e = q8::launch_mma(mode, wb, n, k, r, shi, slo, ssc, sres, sy, n, st);
+        } else if (mode == Q8_ACT_F32 && q8::f64_mma_supports(n, k, r, sx)) {
+            e = q8::launch_f64_mma(wb, n, k, r, sx, sres, sy, n, st);
         } else {
             // the GEMV family, 8 rows at a time
             e = hipSuccess;

@@ -1,0 +1,234 @@
+// f64mma.hip -- the f32 activation mode (f64 sums) for stacks of 5..64 rows on
+// gfx950's f64 matrix cores, every weight block read once for the whole stack
+// (codegen_cuda::lane page, description: f32 activations with f64 sums, every
+// projection reading its weights once; model::author page, Functions: prefill,
+// decode_batch).
+//
+// v_mfma_f64_16x16x4f64 multiplies a 16 x 4 operand A by a 4 x 16 operand B.
+// Here A is 16 activation rows and B 16 weight rows: lane l supplies row l % 16
+// at column l / 16 of either, and gets back the results of activation rows
+// l / 16 + 4 v (v = 0..3) against weight row l % 16.  A block's 32 columns are
+// dealt so that lane l's column at step s is 8 (l / 16) + s: every lane needs 8
+// consecutive quants of its weight row and 8 consecutive f32 values of its
+// activation row.  int8 and f32 values are exact in f64 and so are their
+// products (at most 32 significant bits), so each block's p = sum_j q_j x_j is
+// summed in f64 by 8 chained MFMAs, and d * p joins the output's f64
+// accumulator with one fused multiply-add: the block sum, then the scale, as
+// the numerics define the f32 mode.  Each output is rounded to f32 once, after
+// the residual is added in f64.
+//
+// Work split: one workgroup per 16-row weight tile.  Its 8 waves take the
+// blocks of k in turn (wave g: blocks g, g + 8, ...) for every activation tile
+// of the stack, so each weight block is read by one wave of one workgroup; the
+// waves' partial sums are added in wave order at the end.  Operands come from
+// memory with range-checked buffer loads, a chunk of D blocks ahead of the
+// MFMAs.  Every workgroup reads the stack (through L2); the weights once.
+#include <algorithm>
+
+#include "device.h"
+#include "launch.h"
+
+namespace q8 {
+namespace {
+
+constexpr int kWaves = 8;                 // K groups per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr uint32_t kBufferDword3 = 0x00020000u;
+constexpr int64_t kMaxWeightBytes = int64_t(1) << 30;  // one launch's weights
+constexpr int64_t kMaxK = int64_t(1) << 22;           // keeps 65 rows of x under 2^31 bytes
+// Below 5 rows the f64 GEMV is faster (4 rows of 4096 x 4096: 14 us against
+// 20 us here); from 5 rows on it falls behind (43 us at 6 rows).
+constexpr int kMinRows = 5;
+
+typedef double v4d __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct F64Args {
+    const uint8_t *w;        // Q8_0 blocks [n][nb] of this launch's rows
+    const float *x;          // [rows][k]
+    const float *residual;   // [rows][ldy] or null
+    float *y;                // [rows][ldy]
+    int64_t ldy;
+    uint32_t n;              // weight rows of this launch
+    uint32_t k;
+    uint32_t nb;
+    uint32_t w_bytes;        // n * nb * 34
+    int rows;                // activation rows (5..64)
+};
+
+// One block's operands for this lane: the dword-aligned 12 bytes holding its 8
+// quants, the block's binary16 scale, and 8 f32 activation values per
+// activation tile.
+template <int AT>
+struct Ops {
+    u32x3 win;
+    uint32_t d;
+    f32x4 x[AT][2];
+};
+
+// Block b of weight row `row` for this lane (`live` false: every load reads
+// zeros).  The lane's quants start at byte 2 + 8 (lane / 16) of the block; the
+// 12 bytes from the dword at or before them never reach past the matrix, since
+// k is a multiple of 64 and the last block of a row starts 2 bytes past a dword
+// boundary.
+template <int AT>
+__device__ __forceinline__ void load_ops(const F64Args &a, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx,
+                                         uint32_t row, uint32_t b, int lane, bool live, Ops<AT> &o) {
+    const uint32_t kq = static_cast<uint32_t>(lane >> 4), r16 = static_cast<uint32_t>(lane & 15);
+    const uint32_t blk = row * a.nb + b;
+    const uint32_t dead = oob_bit(live && row < a.n);
+    o.win = __builtin_amdgcn_raw_buffer_load_b96(rw, ((blk * kBlockBytes + 8 * kq) & ~3u) | dead, 0, 0);
+    o.d = __builtin_amdgcn_raw_buffer_load_b16(rw, (blk * kBlockBytes) | dead, 0, 0);
+#pragma unroll
+    for (int t = 0; t < AT; ++t) {
+        const uint32_t r = static_cast<uint32_t>(t * 16) + r16;
+        const uint32_t off = ((r * a.k + b * kBlock + 8 * kq) * 4) | oob_bit(live && r < static_cast<uint32_t>(a.rows));
+        o.x[t][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+        o.x[t][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0);
+    }
+}
+
+// d * (sum of the block's 32 products) into acc, for every activation tile.
+// Block b's parity decides where its quants sit in the window (the window
+// starts at the block when b is even, 2 bytes before it when odd).
+template <int AT>
+__device__ __forceinline__ void math_block(const Ops<AT> &o, uint32_t b, v4d (&acc)[AT]) {
+    const uint32_t sel = window_selector(b);
+    const uint32_t lo = __builtin_amdgcn_perm(o.win.y, o.win.x, sel);
+    const uint32_t hi = __builtin_amdgcn_perm(o.win.z, o.win.y, sel);
+    double q[8];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        q[s] = static_cast<double>(static_cast<int8_t>(lo >> (8 * s)));
+        q[4 + s] = static_cast<double>(static_cast<int8_t>(hi >> (8 * s)));
+    }
+    const double d = static_cast<double>(f16_bits_to_float(o.d & 0xffffu));
+#pragma unroll
+    for (int t = 0; t < AT; ++t) {
+        const float xs[8] = {o.x[t][0].x, o.x[t][0].y, o.x[t][0].z, o.x[t][0].w,
+                             o.x[t][1].x, o.x[t][1].y, o.x[t][1].z, o.x[t][1].w};
+        v4d p = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            p = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(xs[s]), q[s], p, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fma(d, p[v], acc[t][v]);
+    }
+}
+
+template <int AT>
+__global__ __launch_bounds__(kThreads) void f64_mma_kernel(F64Args a) {
+    constexpr int D = 8 / AT;  // blocks per chunk: 64 MFMAs of work between a chunk's loads and its use
+    __shared__ double park[kWaves - 1][AT][4][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t row = blockIdx.x * 16u + static_cast<uint32_t>(lane & 15);
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.w), 0, a.w_bytes, kBufferDword3);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a.x), 0, static_cast<uint32_t>(a.rows) * a.k * 4, kBufferDword3);
+
+    v4d acc[AT];
+#pragma unroll
+    for (int t = 0; t < AT; ++t) acc[t] = v4d{0.0, 0.0, 0.0, 0.0};
+
+    // this wave's blocks: wave + kWaves j for j < mine, in chunks of D blocks
+    // loaded into two register buffers in turn, each chunk's loads issued
+    // before the previous chunk's MFMAs (the scheduler barriers keep that
+    // order).  Blocks past the wave's last read zeros and add exact zeros.
+    const int nb = static_cast<int>(a.nb);
+    const int mine = wave < nb ? (nb - wave + kWaves - 1) / kWaves : 0;
+    const int last = std::max(mine - 1, 0);
+    auto block_of = [&](int j) { return static_cast<uint32_t>(wave + kWaves * std::min(j, last)); };
+    Ops<AT> ping[D], pong[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) load_ops<AT>(a, rw, rx, row, block_of(c), lane, c < mine, ping[c]);
+    for (int j0 = 0; j0 < mine; j0 += 2 * D) {
+#pragma unroll
+        for (int c = 0; c < D; ++c)
+            load_ops<AT>(a, rw, rx, row, block_of(j0 + D + c), lane, j0 + D + c < mine, pong[c]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < D; ++c) math_block<AT>(ping[c], block_of(j0 + c), acc);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < D; ++c)
+            load_ops<AT>(a, rw, rx, row, block_of(j0 + 2 * D + c), lane, j0 + 2 * D + c < mine, ping[c]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j0 + D < mine) {
+#pragma unroll
+            for (int c = 0; c < D; ++c) math_block<AT>(pong[c], block_of(j0 + D + c), acc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // partial sums of waves 1..7 through LDS, added to wave 0's in wave order
+    if (wave > 0) {
+#pragma unroll
+        for (int t = 0; t < AT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) park[wave - 1][t][v][lane] = acc[t][v];
+    }
+    __syncthreads();
+    if (wave != 0 || row >= a.n) return;
+#pragma unroll
+    for (int t = 0; t < AT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            double tot = acc[t][v];
+#pragma unroll
+            for (int w = 0; w < kWaves - 1; ++w) tot += park[w][t][v][lane];
+            const int r = t * 16 + (lane >> 4) + 4 * v;
+            if (r >= a.rows) continue;
+            const int64_t o = static_cast<int64_t>(r) * a.ldy + row;
+            const double res = a.residual ? static_cast<double>(a.residual[o]) : 0.0;
+            a.y[o] = static_cast<float>(tot + res);
+        }
+}
+
+template <int AT>
+hipError_t run(const F64Args &a, hipStream_t stream) {
+    const int64_t row_bytes = static_cast<int64_t>(a.nb) * kBlockBytes;
+    const int64_t slice = std::max<int64_t>(16, (kMaxWeightBytes / row_bytes) / 16 * 16);
+    const int64_t n = a.n;
+    for (int64_t r0 = 0; r0 < n; r0 += slice) {
+        F64Args s = a;
+        s.w = a.w + r0 * row_bytes;
+        s.n = static_cast<uint32_t>(std::min(slice, n - r0));
+        s.w_bytes = static_cast<uint32_t>(s.n * row_bytes);
+        s.y = a.y + r0;
+        s.residual = a.residual ? a.residual + r0 : nullptr;
+        const unsigned grid = (s.n + 15) / 16;
+        f64_mma_kernel<AT><<<grid, kThreads, 0, stream>>>(s);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+bool f64_mma_supports(int64_t n, int64_t k, int rows, const void *x) {
+    return rows >= kMinRows && rows <= 64 && n >= 1 && k >= 64 && k % 64 == 0 && k <= kMaxK &&
+           (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+}
+
+hipError_t launch_f64_mma(const uint8_t *w, int64_t n, int64_t k, int rows, const float *x, const float *residual,
+                          float *y, int64_t ldy, hipStream_t stream) {
+    F64Args a;
+    a.w = w;
+    a.x = x;
+    a.residual = residual;
+    a.y = y;
+    a.ldy = ldy;
+    a.n = static_cast<uint32_t>(n);  // per-launch slices are at most 2^30 bytes of rows
+    a.k = static_cast<uint32_t>(k);
+    a.nb = static_cast<uint32_t>(k / kBlock);
+    a.w_bytes = 0;
+    a.rows = rows;
+    if (rows <= 16) return run<1>(a, stream);
+    if (rows <= 32) return run<2>(a, stream);
+    return run<4>(a, stream);
+}
+
+}  // namespace q8

@@ -57,6 +57,15 @@ hipError_t launch_mma_sums(int mode, const uint8_t *w, int64_t n, int64_t k, int
 bool mma_supports(int mode, int64_t n, int64_t k, int rows, const void *w, const void *hi, const void *lo,
                   const void *scale);
 
+// Projection of a stack of 5..64 f32 rows (f32 mode, f64 sums) on the f64
+// MFMA kernel, every weight block read once.  y and residual have row stride
+// ldy.  Needs what f64_mma_supports needs.
+hipError_t launch_f64_mma(const uint8_t *w, int64_t n, int64_t k, int rows, const float *x, const float *residual,
+                          float *y, int64_t ldy, hipStream_t stream);
+// Whether launch_f64_mma serves this stack: 5..64 rows, n >= 1, k a multiple of
+// 64 up to 2^22, x 16-byte aligned.
+bool f64_mma_supports(int64_t n, int64_t k, int rows, const void *x);
+
 // The fixed device array that stands in for the fused arg-max's workspace in
 // q8_matvec_argmax_noalloc: its size, its address on the current device
 // (looked up once per device), and a kernel that clears its counter.

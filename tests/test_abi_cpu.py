@@ -108,6 +108,18 @@ def test_null_pointers():
     assert q8.lib().q8_quantize_weights(None, 4, 256, BASE + MB, None) == NULL
 
 
+def test_integer_stacks_quantized_inside_take_at_most_eight_rows():
+    """x alone in an integer mode is quantized inside one GEMV pass of at most 8
+    rows; a taller stack is refused before anything is enqueued (the caller
+    quantizes it once and passes hi, lo, scale)."""
+    for mode, lo in ((1, None), (2, None)):
+        for rows in (9, 17, 64, 65, 1000):
+            assert _mm(mode=mode, rows=rows, hi=None, lo=lo, scale=None, x=BASE + 96 * MB) == SHAPE
+    # validation still comes first: a bad mode or alignment is named as such
+    assert _mm(mode=3, rows=9, hi=None, lo=None, scale=None, x=BASE + 96 * MB) == MODE
+    assert _mm(mode=1, rows=9, hi=None, lo=None, scale=None, x=BASE + 96 * MB + 4) == ALIGN
+
+
 def test_alignment():
     assert _mv(w=BASE + 2) == ALIGN
     assert _mv(hi=BASE + 16 * MB + 4) == ALIGN
