@@ -390,8 +390,9 @@ def time_graph(g, iters):
 def stream_ceiling(sizes, dev, reps=20):
     """The measured streaming-read ceiling for each byte count: the bare read
     of libq8probe.so (no math, the GEMV's copy form and ring), over rotating
-    buffers like the projections' weight copies, best over its ring depths and
-    occupancies.  Time per launch from graphs of `reps` launches."""
+    buffers like the projections' weight copies, best over its ring depths
+    (2, 4, 8 items a wave) and occupancies (4, 8, 16 waves a CU).  Time per
+    launch from graphs of `reps` launches."""
     import ctypes
     import torch
     from q8_projection_amd import build as q8build
@@ -406,7 +407,7 @@ def stream_ceiling(sizes, dev, reps=20):
         bufs = [torch.empty(size, dtype=torch.uint8, device=dev) for _ in range(copies)]
         best = None
         for ring in (2, 4, 8):
-            for wpc in (8, 16):
+            for wpc in (4, 8, 16):
                 def launch(i, ring=ring, wpc=wpc):
                     rc = lib.q8probe_stream(ctypes.c_void_p(bufs[i % copies].data_ptr()), size, ring, wpc,
                                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))

@@ -104,7 +104,8 @@ q8_status q8_quantize_act(int mode, const float *x, int64_t rows, int64_t k, int
                           float *scale, void *stream);
 
 /* y = W x (+ residual) for ONE activation row: the decode step's projection
- * (codegen_cuda::lane page, description: projections read in place).
+ * (codegen_cuda::lane page, description: quantized projections consumed straight
+ * from the checkpoint).
  *   mode        : q8_act_mode.
  *   w           : Q8_0 blocks of an n x k matrix, 4-byte aligned (device or
  *                 host-mapped memory).

@@ -18,7 +18,7 @@
  *    with one scale per block (model::author page, description: the .q/.s
  *    files); the product consumes those bytes as stored (spatial::streamed page,
  *    description, the paragraph on a weight moving as it is stored; lane page,
- *    description: projections read in place).  A block is 32 consecutive
+ *    description: quantized projections consumed straight from the checkpoint).  A block is 32 consecutive
  *    values of one output row with one binary16 scale, laid out as 34 bytes:
  *    the scale (little-endian) then the 32 int8 values.
  *  - Activation numerics, the lane's `activations` knob (lane page,

@@ -2,7 +2,7 @@
 //
 // A Q8_0 weight is consumed exactly as a checkpoint stores it: 34-byte blocks,
 // a binary16 scale then 32 int8 values (model::author page, description;
-// spatial::streamed page, description: a weight moves as it is stored).  Block g
+// spatial::streamed page, description: weights travel in their stored form).  Block g
 // of the whole matrix (row-major, g = n * nb + b) starts at byte 34 g, so odd
 // blocks start 2 bytes past a dword boundary.  Every lane loads the 9 dwords of
 // the dword-aligned window at or before its block (36 bytes, never past the end

@@ -1,7 +1,7 @@
 // f64mma.hip -- the f32 activation mode (f64 sums) for stacks of 5..64 rows on
 // gfx950's f64 matrix cores, every weight block read once for the whole stack
-// (codegen_cuda::lane page, description: f32 activations with f64 sums, every
-// projection reading its weights once; model::author page, Functions: prefill,
+// (codegen_cuda::lane page, description: the f32 activation numerics and a
+// stack's single pass over each weight; model::author page, Functions: prefill,
 // decode_batch).
 //
 // v_mfma_f64_16x16x4f64 multiplies a 16 x 4 operand A by a 4 x 16 operand B.
@@ -22,7 +22,8 @@
 // of the stack, so each weight block is read by one wave of one workgroup; the
 // waves' partial sums are added in wave order at the end.  Operands come from
 // memory with range-checked buffer loads, a chunk of D blocks ahead of the
-// MFMAs.  Every workgroup reads the stack (through L2); the weights once.
+// MFMAs.  Every workgroup reads the stack (through L2); HBM serves each weight
+// block one time.
 #include <algorithm>
 
 #include "device.h"

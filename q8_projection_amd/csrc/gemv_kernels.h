@@ -4,8 +4,8 @@
 // the block-sum export), so that they compile in parallel.
 //
 // Each weight row is streamed from HBM once for the whole stack (codegen_cuda::
-// lane page, description: every projection reads its weights once for the
-// block; model::author page, Functions: decode_batch).  The pages' own kernel
+// lane page, description: a stacked step passes over each weight a single time;
+// model::author page, Functions: decode_batch).  The pages' own kernel
 // runs four output rows a (32-wide) warp (codegen_cuda::lane page, Modules,
 // plan: rows_a_warp).  Here a 64-wide wave owns a group of MR output rows at a
 // time.  Its lanes stride over the rows' 34-byte blocks, so one wave-wide load
@@ -372,7 +372,7 @@ __device__ __forceinline__ float write_output(const GemvArgs &a, int r, int64_t 
 // ----------------------------------------------------------------- arg-max
 
 // The LM head closes a decode step by picking the next token (model::author
-// page, Functions: the head reads the last row only): argmax_i y[i], the
+// page, Functions: head, decode_step): argmax_i y[i], the
 // lowest i among equal maxima.  Fused into the GEMV epilogue: every workgroup
 // reduces its rows to one (value, row) partial in the workspace; an agent-scope
 // atomic counter tells the last workgroup to finish, which reduces the partials

@@ -3,9 +3,9 @@ distributions of every call, shared by the tests and the benchmark.
 
 Shapes follow the model forms on the pages: a decode step projects one row
 (codegen_cuda::lane page, description), a batched decode step stacks one row per
-sequence and a prefill chunk stacks the chunk's rows, every projection reading
-its weights once for the whole stack; the LM head reads only the last row of a
-prefill chunk (model::author page, Functions: decode_batch, prefill).
+sequence and a prefill chunk stacks the chunk's rows, with one pass over each
+weight per stack; the LM head projects just the final row of a prefill chunk
+(model::author page, Functions: decode_batch, prefill).
 
 W is N x K (out x in).  Weights are N(0, 0.02^2), activations and residuals
 N(0, 1).  Seeds are fixed; outlier rows/channels are picked on stream seed+1000.

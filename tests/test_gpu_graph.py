@@ -1,5 +1,5 @@
 """Graph capture and replay of a decode step's projections (codegen_cuda::lane
-page, description: each step is captured once as a graph and replayed per token).
+page, description: a step is recorded as a graph one time and that graph re-run for every token).
 
 The library enqueues only kernels (no allocation, copy, memset or host
 synchronization), so a sequence of calls captured into a HIP graph must
