@@ -59,12 +59,13 @@ struct F64Args {
 };
 
 // One block's operands for this lane: the dword-aligned 12 bytes holding its 8
-// quants, the block's binary16 scale, and 8 f32 activation values per
-// activation tile.
+// quants and 8 f32 activation values per activation tile.  The block's
+// binary16 scale is not loaded on its own: the window of a row's first lane
+// (lane / 16 == 0) starts at the block or 2 bytes before it, so its first dword
+// holds the scale, which math_block passes to the row's other lanes.
 template <int AT>
 struct Ops {
     u32x3 win;
-    uint32_t d;
     f32x4 x[AT][2];
 };
 
@@ -80,7 +81,6 @@ __device__ __forceinline__ void load_ops(const F64Args &a, __amdgpu_buffer_rsrc_
     const uint32_t blk = row * a.nb + b;
     const uint32_t dead = oob_bit(live && row < a.n);
     o.win = __builtin_amdgcn_raw_buffer_load_b96(rw, ((blk * kBlockBytes + 8 * kq) & ~3u) | dead, 0, 0);
-    o.d = __builtin_amdgcn_raw_buffer_load_b16(rw, (blk * kBlockBytes) | dead, 0, 0);
 #pragma unroll
     for (int t = 0; t < AT; ++t) {
         const uint32_t r = static_cast<uint32_t>(t * 16) + r16;
@@ -92,9 +92,11 @@ __device__ __forceinline__ void load_ops(const F64Args &a, __amdgpu_buffer_rsrc_
 
 // d * (sum of the block's 32 products) into acc, for every activation tile.
 // Block b's parity decides where its quants sit in the window (the window
-// starts at the block when b is even, 2 bytes before it when odd).
+// starts at the block when b is even, 2 bytes before it when odd), and where
+// the scale sits in the first dword of the row's first lane, which every lane
+// of the row reads with ds_bpermute (lane_row4 = 4 (lane % 16)).
 template <int AT>
-__device__ __forceinline__ void math_block(const Ops<AT> &o, uint32_t b, v4d (&acc)[AT]) {
+__device__ __forceinline__ void math_block(const Ops<AT> &o, uint32_t b, int lane_row4, v4d (&acc)[AT]) {
     const uint32_t sel = window_selector(b);
     const uint32_t lo = __builtin_amdgcn_perm(o.win.y, o.win.x, sel);
     const uint32_t hi = __builtin_amdgcn_perm(o.win.z, o.win.y, sel);
@@ -104,7 +106,9 @@ __device__ __forceinline__ void math_block(const Ops<AT> &o, uint32_t b, v4d (&a
         q[s] = static_cast<double>(static_cast<int8_t>(lo >> (8 * s)));
         q[4 + s] = static_cast<double>(static_cast<int8_t>(hi >> (8 * s)));
     }
-    const double d = static_cast<double>(f16_bits_to_float(o.d & 0xffffu));
+    const uint32_t own = (b & 1) ? (o.win.x >> 16) : (o.win.x & 0xffffu);
+    const uint32_t dbits = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(lane_row4, static_cast<int>(own)));
+    const double d = static_cast<double>(f16_bits_to_float(dbits));
 #pragma unroll
     for (int t = 0; t < AT; ++t) {
         const float xs[8] = {o.x[t][0].x, o.x[t][0].y, o.x[t][0].z, o.x[t][0].w,
@@ -123,6 +127,7 @@ __global__ __launch_bounds__(kThreads) void f64_mma_kernel(F64Args a) {
     constexpr int D = 8 / AT;  // blocks per chunk: 64 MFMAs of work between a chunk's loads and its use
     __shared__ double park[kWaves - 1][AT][4][64];
     const int lane = threadIdx.x & 63;
+    const int lane_row4 = (lane & 15) << 2;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t row = blockIdx.x * 16u + static_cast<uint32_t>(lane & 15);
     const __amdgpu_buffer_rsrc_t rw =
@@ -137,7 +142,10 @@ __global__ __launch_bounds__(kThreads) void f64_mma_kernel(F64Args a) {
     // this wave's blocks: wave + kWaves j for j < mine, in chunks of D blocks
     // loaded into two register buffers in turn, each chunk's loads issued
     // before the previous chunk's MFMAs (the scheduler barriers keep that
-    // order).  Blocks past the wave's last read zeros and add exact zeros.
+    // order).  The loop runs while a whole pair of chunks and one more block
+    // remain, so every refill it issues reads at least one live block; the
+    // last one or two chunks are finished after it without refills.  Blocks
+    // past the wave's last read zeros and add exact zeros.
     const int nb = static_cast<int>(a.nb);
     const int mine = wave < nb ? (nb - wave + kWaves - 1) / kWaves : 0;
     const int last = std::max(mine - 1, 0);
@@ -145,23 +153,36 @@ __global__ __launch_bounds__(kThreads) void f64_mma_kernel(F64Args a) {
     Ops<AT> ping[D], pong[D];
 #pragma unroll
     for (int c = 0; c < D; ++c) load_ops<AT>(a, rw, rx, row, block_of(c), lane, c < mine, ping[c]);
-    for (int j0 = 0; j0 < mine; j0 += 2 * D) {
+    int j0 = 0;
+    for (; j0 + 2 * D < mine; j0 += 2 * D) {
 #pragma unroll
         for (int c = 0; c < D; ++c)
             load_ops<AT>(a, rw, rx, row, block_of(j0 + D + c), lane, j0 + D + c < mine, pong[c]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < D; ++c) math_block<AT>(ping[c], block_of(j0 + c), acc);
+        for (int c = 0; c < D; ++c) math_block<AT>(ping[c], block_of(j0 + c), lane_row4, acc);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < D; ++c)
             load_ops<AT>(a, rw, rx, row, block_of(j0 + 2 * D + c), lane, j0 + 2 * D + c < mine, ping[c]);
         __builtin_amdgcn_sched_barrier(0);
-        if (j0 + D < mine) {
 #pragma unroll
-            for (int c = 0; c < D; ++c) math_block<AT>(pong[c], block_of(j0 + D + c), acc);
-        }
+        for (int c = 0; c < D; ++c) math_block<AT>(pong[c], block_of(j0 + D + c), lane_row4, acc);
         __builtin_amdgcn_sched_barrier(0);
+    }
+    if (j0 + D < mine) {  // two chunks left: chunk j0 is in ping
+#pragma unroll
+        for (int c = 0; c < D; ++c)
+            load_ops<AT>(a, rw, rx, row, block_of(j0 + D + c), lane, j0 + D + c < mine, pong[c]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < D; ++c) math_block<AT>(ping[c], block_of(j0 + c), lane_row4, acc);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < D; ++c) math_block<AT>(pong[c], block_of(j0 + D + c), lane_row4, acc);
+    } else if (j0 < mine) {  // one chunk left
+#pragma unroll
+        for (int c = 0; c < D; ++c) math_block<AT>(ping[c], block_of(j0 + c), lane_row4, acc);
     }
 
     // partial sums of waves 1..7 through LDS, added to wave 0's in wave order

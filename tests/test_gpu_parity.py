@@ -572,6 +572,23 @@ def test_f32_stacks_at_full_size(n, k, rows, with_res):
     say("f32 stack", f"max rel err {rel:.3g}", f"max ulps {ulps}")
 
 
+@pytest.mark.parametrize("n,k,rows", [(37, 64, 9), (20, 128, 16), (300, 192, 33), (16, 64, 64), (1, 256, 5),
+                                      (17, 320, 48)])
+def test_f32_stacks_with_short_k(n, k, rows):
+    """f32 stacks whose k gives fewer blocks than the f64 MFMA kernel has waves
+    (k = 64: two blocks for eight waves), odd block counts per wave, and a
+    weight tile with a single row or a ragged last tile."""
+    say("f32 stack, short k", n, k, rows)
+    w = synth.weights(n, k, seed=2900 + k, outlier_frac=0.05)
+    x = synth.activations(rows, k, seed=2950 + rows, outlier_frac=0.05)
+    res = synth.normal(2990, (rows, n))
+    blocks = oracle.quantize_weights(w)
+    call = workloads.Call("f32_short_k", n, k, rows, "f32", "matmul_rows", w_seed=0)
+    y, *_ = gpu_path(call, to_dev(blocks), x, res)
+    (r, a), _ = oracle_path(call, blocks, x, res)
+    gate(y, r, a, f"f32 short k {n}x{k} rows={rows}")
+
+
 def test_f32_stack_rows_do_not_depend_on_the_stack():
     """On the f64 MFMA kernel each output is one lane's f64 total over the
     blocks, in an order fixed by k alone (block sums from chained MFMAs, then
