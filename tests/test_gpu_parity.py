@@ -354,6 +354,63 @@ def test_argmax_fused_into_the_projection(n, k, mode, with_res, inside):
         assert int(idx.item()) == int(top[0])
 
 
+@pytest.mark.parametrize("n,k,mode,calls", [(151936, 2048, "i8", 48), (20000, 1024, "i8x2", 96)])
+def test_argmax_many_calls_in_a_row(n, k, mode, calls):
+    """The arg-max's hand-off between workgroups (partials posted with
+    agent-scope stores, an atomic arrival counter, the last workgroup reading
+    the partials) over many launches queued back to back on one stream and one
+    workspace, with no host synchronisation between them: each call projects a
+    different activation row, so the maximum moves from call to call.  Every
+    call's index must be the first maximum of its own y, every y the plain
+    projection's, and the counter back at zero at the end.  Then the same
+    sequence captured in a HIP graph and replayed three times."""
+    say("argmax calls in a row", n, k, mode, calls)
+    w = synth.weights(n, k, seed=2100 + n % 89)
+    xs = synth.activations(calls, k, seed=2200 + calls, outlier_frac=0.01)
+    wd = to_dev(oracle.quantize_weights(w))
+    hi, lo, sc = q8.quantize_act(mode, to_dev(xs))
+    work = torch.zeros(q8.argmax_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    ys = torch.empty((calls, n), dtype=torch.float32, device="cuda")
+    idx = torch.full((calls,), -1, dtype=torch.int32, device="cuda")
+
+    def run_all():
+        for c in range(calls):
+            q8.matvec_argmax(mode, wd, n, k, hi=hi[c], lo=None if lo is None else lo[c], scale=sc[c],
+                             out=ys[c], idx=idx[c:c + 1], workspace=work)
+
+    def check(tag):
+        first_max = torch.argmax((ys == ys.max(dim=1, keepdim=True).values).to(torch.int32), dim=1)
+        assert torch.equal(idx.to(torch.int64), first_max), tag
+        assert int(work[:16].count_nonzero().item()) == 0, tag
+
+    run_all()
+    torch.cuda.synchronize()
+    plain = torch.stack([q8.matvec(mode, wd, n, k, hi=hi[c], lo=None if lo is None else lo[c], scale=sc[c])
+                         for c in range(calls)])
+    torch.cuda.synchronize()
+    assert torch.equal(ys, plain)
+    check("eager")
+    assert len(set(idx.tolist())) > 1  # the maximum does move between calls
+    ref_idx = idx.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run_all()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ys.zero_()
+        idx.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ys, plain), rep
+        assert torch.equal(idx, ref_idx), rep
+        check(f"replay {rep}")
+
+
 def test_argmax_ties_go_to_the_lowest_index():
     n, k = 4000, 2048
     say("argmax ties", n, k)
