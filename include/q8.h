@@ -132,13 +132,17 @@ q8_status q8_matvec(int mode, const void *w, int64_t n, int64_t k, const int8_t 
 /* Y = X W^T (+ residual) for a stack of `rows` activation rows, every weight
  * block read once per stack of up to 64 rows: a batched decode step (one row a
  * sequence) or a prefill chunk (model::author page, Functions: decode_batch,
- * prefill; codegen_cuda::lane page, description: chunks of 2, 4, ... rows).
+ * prefill; codegen_cuda::lane page, description: prefill chunks of power-of-two
+ * row counts).
  * Arguments as q8_matvec with [rows][...] stacks: hi/lo/x [rows][k],
  * scale [rows][k/32], residual and y [rows][n].  rows >= 1; stacks wider than
  * 64 rows are run as consecutive 64-row slices.  Kernels: integer stacks of
  * 2..64 rows on int8 MFMA tiles (or the GEMV for short stacks), f32 stacks of
  * 5..64 rows on f64 MFMA tiles (sums still exact products added in f64), up to
- * 4 rows on the GEMV; each slice streams the weights once.  An integer-mode
+ * 4 rows on the GEMV; each slice streams the weights once.  Two cases fall back
+ * to the GEMV 8 rows at a time, reading the weights once per 8 rows: integer
+ * stacks whose k is not a multiple of 256 or whose weights reach 1 GiB, and f32
+ * stacks with k above 2^22.  An integer-mode
  * stack given as x (hi, lo, scale NULL) is quantized inside the projection as
  * in q8_matvec, for at most 8 rows (one GEMV pass); a taller one is
  * Q8_E_SHAPE: quantize it once with q8_quantize_act (the result serves every
