@@ -141,8 +141,8 @@ q8_status q8_matvec(int mode, const void *w, int64_t n, int64_t k, const int8_t 
  * 5..64 rows on f64 MFMA tiles (sums still exact products added in f64), up to
  * 4 rows on the GEMV; each slice streams the weights once.  Two cases fall back
  * to the GEMV 8 rows at a time, reading the weights once per 8 rows: integer
- * stacks whose k is not a multiple of 256 or whose weights reach 1 GiB, and f32
- * stacks with k above 2^22.  An integer-mode
+ * stacks whose k is not a multiple of 256 or whose weights or stack are not
+ * 16-byte aligned, and f32 stacks with k above 2^22.  An integer-mode
  * stack given as x (hi, lo, scale NULL) is quantized inside the projection as
  * in q8_matvec, for at most 8 rows (one GEMV pass); a taller one is
  * Q8_E_SHAPE: quantize it once with q8_quantize_act (the result serves every

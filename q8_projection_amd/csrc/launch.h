@@ -53,7 +53,8 @@ hipError_t launch_mma_sums(int mode, const uint8_t *w, int64_t n, int64_t k, int
 // 2 rows on a matrix of at most 16 rows per CU, or whose row ranges fill at
 // least three quarters of their MFMA tiles (two-word) or whole 64-row ranges
 // (one-word); the GEMV is faster for the other 2-row stacks), k a multiple of
-// 256, weights under 1 GiB, and weights, words and scales 16-byte aligned.
+// 256, and weights, words and scales 16-byte aligned.  Weights of 1 GiB or more
+// run as row slices of under 1 GiB, one launch each.
 bool mma_supports(int mode, int64_t n, int64_t k, int rows, const void *w, const void *hi, const void *lo,
                   const void *scale);
 

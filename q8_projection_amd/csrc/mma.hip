@@ -19,7 +19,8 @@ bool mma_supports(int mode, int64_t n, int64_t k, int rows, const void *w, const
     const bool one_tile = per_wg <= 16;
     const bool two_rows = one_tile || (mode == 2 ? 4 * per_wg >= 3 * tile_rows : per_wg == 64);
     if (rows == 2 && !two_rows) return false;
-    if (n * (k / kBlock) * kBlockBytes > (int64_t(1) << 30)) return false;
+    // launches take row slices under 1 GiB of weights; a 16-row slice must fit
+    if (16 * (k / kBlock) * kBlockBytes > (int64_t(1) << 30)) return false;
     const auto al16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
     if (!al16(w) || !al16(hi) || !al16(scale) || (mode == 2 && !al16(lo))) return false;
     return true;

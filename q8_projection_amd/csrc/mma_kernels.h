@@ -65,6 +65,7 @@ constexpr uint32_t kOob = 0x80000000u;
 constexpr int kWaveMaxRt = 1;     // single-tile stacks on matrices this short use the wave-private kernel
 constexpr int kWaveWaves = 8;
 constexpr int kWaveDepth = 2;
+constexpr int64_t kMaxMmaWeightBytes = int64_t(1) << 30;  // one launch's weights (buffer offsets < 2^31)
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t *lds_ptr_t;
@@ -126,7 +127,8 @@ struct MmaArgs {
     int rows_per_wg;
     int nchunks;             // nb / 8
     uint32_t lo_oob;         // kOob for a one-word stack run in the two-word layout, else 0
-    int32_t *sums;           // block-sum export [rows][n][nb][sums_words], or null
+    int32_t *sums;           // block-sum export [rows][sums_ld][nb][sums_words], or null
+    int64_t sums_ld;         // weight rows of the whole call (the export's row stride)
     int sums_words;          // 2 for a two-word stack, else 1
 };
 
@@ -325,14 +327,14 @@ __device__ __forceinline__ void export_sums(const MmaArgs &a, const v4i &sum, in
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             if (ar + i >= a.rows) continue;
-            int32_t *o = a.sums + ((static_cast<int64_t>(ar + i) * a.n + n) * a.nb + blk) * a.sums_words;
+            int32_t *o = a.sums + ((static_cast<int64_t>(ar + i) * a.sums_ld + n) * a.nb + blk) * a.sums_words;
             o[0] = sum[2 * i];
             if (a.sums_words == 2) o[1] = sum[2 * i + 1];
         }
     } else {
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-            if (ar + v < a.rows) a.sums[(static_cast<int64_t>(ar + v) * a.n + n) * a.nb + blk] = sum[v];
+            if (ar + v < a.rows) a.sums[(static_cast<int64_t>(ar + v) * a.sums_ld + n) * a.nb + blk] = sum[v];
     }
 }
 
@@ -707,10 +709,12 @@ int act_tiles(int words, int rows) {
 
 // The kernel and wave split for a call (shared by the projection and the
 // block-sum export, so that the export runs the projection's kernel).
+// One launch over n weight rows (under 1 GiB of weights).  sums: this launch's
+// first row of the export, whose row stride is sums_ld.
 template <bool SUMS>
-hipError_t launch_mma_impl(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
-                           const int8_t *lo, const float *scale, const float *residual, float *y, int64_t ldy,
-                           int32_t *sums, hipStream_t stream) {
+hipError_t launch_mma_slice(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
+                            const int8_t *lo, const float *scale, const float *residual, float *y, int64_t ldy,
+                            int32_t *sums, int64_t sums_ld, hipStream_t stream) {
     // One-word stacks of up to eight rows run in the two-word layout with their
     // lo words read as zeros: T = 128 S_hi is exact, the final 1/128 undoes the
     // factor (a power of two: the f64 sums carry the same bits scaled), and a
@@ -741,6 +745,7 @@ hipError_t launch_mma_impl(int mode, const uint8_t *w, int64_t n, int64_t k, int
     a.rows_per_wg = static_cast<int>(per_wg);
     a.nchunks = static_cast<int>(nb / kChunkBlocks);
     a.sums = sums;
+    a.sums_ld = sums_ld;
     a.sums_words = mode == 2 ? 2 : 1;
     if (at == 1 && rt <= kWaveMaxRt) {
         if (words == 2) return run_wave<2, kWaveWaves, kWaveDepth, SUMS>(a, stream);
@@ -759,6 +764,28 @@ hipError_t launch_mma_impl(int mode, const uint8_t *w, int64_t n, int64_t k, int
         case 2: return by_rt<1, 2, SUMS>(rt, a, stream);
         default: return by_rt<1, 4, SUMS>(rt, a, stream);
     }
+}
+
+// The projection (or its block-sum export) over all n weight rows: launches
+// over row slices of under 1 GiB of weights each (buffer offsets stay below
+// 2^31), each reading its rows once; y, residual and the export are addressed
+// with the whole call's row strides.
+template <bool SUMS>
+hipError_t launch_mma_impl(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
+                           const int8_t *lo, const float *scale, const float *residual, float *y, int64_t ldy,
+                           int32_t *sums, hipStream_t stream) {
+    const int64_t nb = k / kBlock;
+    const int64_t row_bytes = nb * kBlockBytes;
+    const int64_t slice = std::max<int64_t>(16, (kMaxMmaWeightBytes / row_bytes) / 16 * 16);
+    const int64_t words = mode == 2 ? 2 : 1;
+    for (int64_t n0 = 0; n0 < n; n0 += slice) {
+        const int64_t ns = std::min(slice, n - n0);
+        const hipError_t e = launch_mma_slice<SUMS>(mode, w + n0 * row_bytes, ns, k, rows, hi, lo, scale,
+                                                    residual ? residual + n0 : nullptr, y ? y + n0 : nullptr, ldy,
+                                                    sums ? sums + n0 * nb * words : nullptr, n, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace

@@ -607,6 +607,42 @@ def test_f32_row_on_both_grids(n, k, with_res):
     gate(y.cpu().numpy()[None], r, a, f"f32 {n}x{k}")
 
 
+# ------------------------------------------------------------ weights over 1 GiB
+
+@pytest.mark.parametrize("mode,rows", [("i8x2", 9), ("i8", 16)])
+def test_stacks_over_1gib_of_weights(mode, rows):
+    """A 32768x32768 Q8_0 matrix (1.06 GiB) runs on the int8 MFMA kernels as two
+    row slices of under 1 GiB (rows 0..30831 and 30832..32767).  Outputs on
+    both sides of the boundary and at random places match the oracle one by one;
+    block sums of rows at both ends of each slice match it bit for bit.  The
+    blocks are random bytes from a seeded generator: binary16 scales drawn
+    around 1e-3, quants uniform in [-127, 127]."""
+    n = k = 32768
+    say("over 1 GiB", mode, rows, n, k)
+    rng = np.random.default_rng(3100 + rows)
+    nb = k // 32
+    blocks = np.empty((n, nb, 34), dtype=np.uint8)
+    scales = (np.abs(rng.standard_normal((n, nb))) * 1e-3 + 1e-4).astype(np.float16)
+    blocks[:, :, 0:2] = scales.view(np.uint8).reshape(n, nb, 2)
+    blocks[:, :, 2:] = rng.integers(-127, 128, size=(n, nb, 32), dtype=np.int8).view(np.uint8)
+    blocks = blocks.reshape(n, nb * 34)
+    x = synth.activations(rows, k, seed=3200 + rows, outlier_frac=0.01)
+    wd = to_dev(blocks)
+    hi, lo, sc = q8.quantize_act(mode, to_dev(x))
+    y = q8.matmul_rows(mode, wd, n, k, hi=hi, lo=lo, scale=sc)
+    edge_rows = np.array([0, 1, 30830, 30831, 30832, 30833, 32766, 32767])
+    sums = q8.block_sums(mode, wd, n, k, hi, lo)
+    torch.cuda.synchronize()
+    ohi, olo, osc = oracle.quantize_act(mode, x)
+    r_idx = np.concatenate([np.repeat(np.arange(rows), edge_rows.size), rng.integers(0, rows, 512)])
+    n_idx = np.concatenate([np.tile(edge_rows, rows), rng.integers(0, n, 512)])
+    ry, ra = oracle.project_at(mode, blocks, n, k, rows, r_idx, n_idx, hi=ohi, lo=olo, scale=osc)
+    got = y.cpu().numpy()[r_idx, n_idx]
+    gate(got[None], ry[None], ra[None], f"over 1 GiB {mode} rows={rows}")
+    want = oracle.block_sums(mode, blocks[edge_rows], edge_rows.size, k, ohi, olo)
+    assert np.array_equal(sums[:, torch.from_numpy(edge_rows).cuda()].cpu().numpy(), want)
+
+
 # ------------------------------------------------------------ f32 stacks, f64 MFMA tiles
 
 @pytest.mark.parametrize("n,k,rows,with_res", [(14336, 4096, 64, False), (4096, 14336, 16, True),
