@@ -242,9 +242,13 @@ def time_head_argmax(p, reps):
     work = torch.zeros(q8.argmax_workspace_bytes(c.n), dtype=torch.uint8, device=y.device)
     out = torch.empty_like(y)
 
+    # the same activation input as the plain head: the f32 row when its
+    # quantization runs inside the projection, else the quantized row
+    act = (dict(x=p.x[0]) if p.inside else
+           dict(hi=p.hi[0], lo=None if p.lo is None else p.lo[0], scale=p.sc[0]))
+
     def launch(i):
-        q8.matvec_argmax(c.mode, p.w[i % p.copies], c.n, c.k, hi=p.hi[0], scale=p.sc[0], out=out, idx=idx,
-                         workspace=work)
+        q8.matvec_argmax(c.mode, p.w[i % p.copies], c.n, c.k, out=out, idx=idx, workspace=work, **act)
 
     g = capture(lambda: [launch(i) for i in range(reps)])
     t = time_graph(g, 5) / reps
