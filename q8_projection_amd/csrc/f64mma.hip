@@ -38,7 +38,7 @@ constexpr uint32_t kBufferDword3 = 0x00020000u;
 constexpr int64_t kMaxWeightBytes = int64_t(1) << 30;  // one launch's weights
 constexpr int64_t kMaxK = int64_t(1) << 22;           // keeps 65 rows of x under 2^31 bytes
 // Below 5 rows the f64 GEMV is faster (4 rows of 4096 x 4096: 14 us against
-// 20 us here); from 5 rows on it falls behind (43 us at 6 rows).
+// about 16 us here); from 5 rows on it falls far behind (43 us at 6 rows).
 constexpr int kMinRows = 5;
 
 typedef double v4d __attribute__((ext_vector_type(4)));
