@@ -609,38 +609,60 @@ def test_f32_row_on_both_grids(n, k, with_res):
 
 # ------------------------------------------------------------ weights over 1 GiB
 
-@pytest.mark.parametrize("mode,rows", [("i8x2", 9), ("i8", 16)])
+_BIG_BLOCKS = {}
+
+
+def _big_blocks():
+    """A 32768x32768 Q8_0 matrix (1.06 GiB) of random bytes from a seeded
+    generator: binary16 scales drawn around 1e-3, quants uniform in [-127, 127].
+    Built once for the module."""
+    if "b" not in _BIG_BLOCKS:
+        n = k = 32768
+        rng = np.random.default_rng(3100)
+        nb = k // 32
+        blocks = np.empty((n, nb, 34), dtype=np.uint8)
+        scales = (np.abs(rng.standard_normal((n, nb))) * 1e-3 + 1e-4).astype(np.float16)
+        blocks[:, :, 0:2] = scales.view(np.uint8).reshape(n, nb, 2)
+        blocks[:, :, 2:] = rng.integers(-127, 128, size=(n, nb, 32), dtype=np.int8).view(np.uint8)
+        _BIG_BLOCKS["b"] = blocks.reshape(n, nb * 34)
+    return _BIG_BLOCKS["b"]
+
+
+@pytest.mark.parametrize("mode,rows", [("i8x2", 9), ("i8", 16), ("i8x2", 1), ("i8", 2), ("f32", 1), ("f32", 5)])
 def test_stacks_over_1gib_of_weights(mode, rows):
-    """A 32768x32768 Q8_0 matrix (1.06 GiB) runs on the int8 MFMA kernels as two
-    row slices of under 1 GiB (rows 0..30831 and 30832..32767).  Outputs on
-    both sides of the boundary and at random places match the oracle one by one;
-    block sums of rows at both ends of each slice match it bit for bit.  The
-    blocks are random bytes from a seeded generator: binary16 scales drawn
-    around 1e-3, quants uniform in [-127, 127]."""
+    """Weights of 1.06 GiB (32768x32768): every kernel family runs it as row
+    slices of at most 1 GiB, one launch each (the MFMA kernels: rows 0..30831
+    and 30832..32767; the resident GEMV: 0..30839 and 30840..32767; the tiled
+    GEMV addresses each row group from its own base).  Outputs on both sides of the slice boundaries
+    and at random places match the oracle one by one; in the integer modes the
+    block sums of rows at the ends of the slices match it bit for bit."""
     n = k = 32768
     say("over 1 GiB", mode, rows, n, k)
-    rng = np.random.default_rng(3100 + rows)
-    nb = k // 32
-    blocks = np.empty((n, nb, 34), dtype=np.uint8)
-    scales = (np.abs(rng.standard_normal((n, nb))) * 1e-3 + 1e-4).astype(np.float16)
-    blocks[:, :, 0:2] = scales.view(np.uint8).reshape(n, nb, 2)
-    blocks[:, :, 2:] = rng.integers(-127, 128, size=(n, nb, 32), dtype=np.int8).view(np.uint8)
-    blocks = blocks.reshape(n, nb * 34)
+    blocks = _big_blocks()
+    rng = np.random.default_rng(3300 + rows)
     x = synth.activations(rows, k, seed=3200 + rows, outlier_frac=0.01)
     wd = to_dev(blocks)
-    hi, lo, sc = q8.quantize_act(mode, to_dev(x))
-    y = q8.matmul_rows(mode, wd, n, k, hi=hi, lo=lo, scale=sc)
-    edge_rows = np.array([0, 1, 30830, 30831, 30832, 30833, 32766, 32767])
-    sums = q8.block_sums(mode, wd, n, k, hi, lo)
-    torch.cuda.synchronize()
-    ohi, olo, osc = oracle.quantize_act(mode, x)
+    xd = to_dev(x)
+    # slice ends: 30832 rows (int8 and f64 MFMA, multiples of 16), 30840 (GEMV)
+    edge_rows = np.array([0, 1, 30831, 30832, 30833, 30839, 30840, 30841, 32766, 32767])
     r_idx = np.concatenate([np.repeat(np.arange(rows), edge_rows.size), rng.integers(0, rows, 512)])
     n_idx = np.concatenate([np.tile(edge_rows, rows), rng.integers(0, n, 512)])
-    ry, ra = oracle.project_at(mode, blocks, n, k, rows, r_idx, n_idx, hi=ohi, lo=olo, scale=osc)
+    if mode == "f32":
+        y = q8.matmul_rows(mode, wd, n, k, x=xd)
+        torch.cuda.synchronize()
+        ry, ra = oracle.project_at(mode, blocks, n, k, rows, r_idx, n_idx, x=x)
+    else:
+        hi, lo, sc = q8.quantize_act(mode, xd)
+        y = q8.matmul_rows(mode, wd, n, k, hi=hi, lo=lo, scale=sc)
+        sums = q8.block_sums(mode, wd, n, k, hi, lo)
+        torch.cuda.synchronize()
+        ohi, olo, osc = oracle.quantize_act(mode, x)
+        ry, ra = oracle.project_at(mode, blocks, n, k, rows, r_idx, n_idx, hi=ohi, lo=olo, scale=osc)
+        want = oracle.block_sums(mode, blocks[edge_rows], edge_rows.size, k, ohi, olo)
+        assert np.array_equal(sums[:, torch.from_numpy(edge_rows).cuda()].cpu().numpy(), want)
+        del sums
     got = y.cpu().numpy()[r_idx, n_idx]
     gate(got[None], ry[None], ra[None], f"over 1 GiB {mode} rows={rows}")
-    want = oracle.block_sums(mode, blocks[edge_rows], edge_rows.size, k, ohi, olo)
-    assert np.array_equal(sums[:, torch.from_numpy(edge_rows).cuda()].cpu().numpy(), want)
 
 
 # ------------------------------------------------------------ f32 stacks, f64 MFMA tiles
