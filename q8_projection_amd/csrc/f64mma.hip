@@ -58,29 +58,34 @@ struct F64Args {
     int rows;                // activation rows (5..64)
 };
 
-// One block's operands for this lane: the dword-aligned 12 bytes holding its 8
-// quants and 8 f32 activation values per activation tile.  The block's
-// binary16 scale is not loaded on its own: the window of a row's first lane
-// (lane / 16 == 0) starts at the block or 2 bytes before it, so its first dword
-// holds the scale, which math_block passes to the row's other lanes.
-template <int AT>
+// One block's operands for this lane: for each of its RT weight rows the
+// dword-aligned 12 bytes holding its 8 quants, and 8 f32 activation values per
+// activation tile.  The block's binary16 scale is not loaded on its own: the
+// window of a row's first lane (lane / 16 == 0) starts at the block or 2 bytes
+// before it, so its first dword holds the scale, which math_block passes to the
+// row's other lanes.
+template <int RT, int AT>
 struct Ops {
-    u32x3 win;
+    u32x3 win[RT];
     f32x4 x[AT][2];
 };
 
-// Block b of weight row `row` for this lane (`live` false: every load reads
-// zeros).  The lane's quants start at byte 2 + 8 (lane / 16) of the block; the
-// 12 bytes from the dword at or before them never reach past the matrix, since
-// k is a multiple of 64 and the last block of a row starts 2 bytes past a dword
-// boundary.
-template <int AT>
+// Block b of weight rows row + 16 rt for this lane (`live` false: every load
+// reads zeros).  The lane's quants start at byte 2 + 8 (lane / 16) of the
+// block; the 12 bytes from the dword at or before them never reach past the
+// matrix, since k is a multiple of 64 and the last block of a row starts 2
+// bytes past a dword boundary.
+template <int RT, int AT>
 __device__ __forceinline__ void load_ops(const F64Args &a, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx,
-                                         uint32_t row, uint32_t b, int lane, bool live, Ops<AT> &o) {
+                                         uint32_t row, uint32_t b, int lane, bool live, Ops<RT, AT> &o) {
     const uint32_t kq = static_cast<uint32_t>(lane >> 4), r16 = static_cast<uint32_t>(lane & 15);
-    const uint32_t blk = row * a.nb + b;
-    const uint32_t dead = oob_bit(live && row < a.n);
-    o.win = __builtin_amdgcn_raw_buffer_load_b96(rw, ((blk * kBlockBytes + 8 * kq) & ~3u) | dead, 0, 0);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const uint32_t wrow = row + 16 * rt;
+        const uint32_t blk = wrow * a.nb + b;
+        const uint32_t dead = oob_bit(live && wrow < a.n);
+        o.win[rt] = __builtin_amdgcn_raw_buffer_load_b96(rw, ((blk * kBlockBytes + 8 * kq) & ~3u) | dead, 0, 0);
+    }
 #pragma unroll
     for (int t = 0; t < AT; ++t) {
         const uint32_t r = static_cast<uint32_t>(t * 16) + r16;
@@ -90,54 +95,70 @@ __device__ __forceinline__ void load_ops(const F64Args &a, __amdgpu_buffer_rsrc_
     }
 }
 
-// d * (sum of the block's 32 products) into acc, for every activation tile.
-// Block b's parity decides where its quants sit in the window (the window
-// starts at the block when b is even, 2 bytes before it when odd), and where
-// the scale sits in the first dword of the row's first lane, which every lane
-// of the row reads with ds_bpermute (lane_row4 = 4 (lane % 16)).
-template <int AT>
-__device__ __forceinline__ void math_block(const Ops<AT> &o, uint32_t b, int lane_row4, v4d (&acc)[AT]) {
+// d * (sum of the block's 32 products) into acc, for every weight and
+// activation tile.  Block b's parity decides where its quants sit in a window
+// (the window starts at the block when b is even, 2 bytes before it when odd),
+// and where the scale sits in the first dword of the row's first lane, which
+// every lane of the row reads with ds_bpermute (lane_row4 = 4 (lane % 16)).
+// Each activation value is converted once and used for every weight tile.
+template <int RT, int AT>
+__device__ __forceinline__ void math_block(const Ops<RT, AT> &o, uint32_t b, int lane_row4, v4d (&acc)[RT][AT]) {
     const uint32_t sel = window_selector(b);
-    const uint32_t lo = __builtin_amdgcn_perm(o.win.y, o.win.x, sel);
-    const uint32_t hi = __builtin_amdgcn_perm(o.win.z, o.win.y, sel);
-    double q[8];
+    double q[RT][8];
+    double d[RT];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        q[s] = static_cast<double>(static_cast<int8_t>(lo >> (8 * s)));
-        q[4 + s] = static_cast<double>(static_cast<int8_t>(hi >> (8 * s)));
+    for (int rt = 0; rt < RT; ++rt) {
+        const uint32_t lo = __builtin_amdgcn_perm(o.win[rt].y, o.win[rt].x, sel);
+        const uint32_t hi = __builtin_amdgcn_perm(o.win[rt].z, o.win[rt].y, sel);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            q[rt][s] = static_cast<double>(static_cast<int8_t>(lo >> (8 * s)));
+            q[rt][4 + s] = static_cast<double>(static_cast<int8_t>(hi >> (8 * s)));
+        }
+        const uint32_t own = (b & 1) ? (o.win[rt].x >> 16) : (o.win[rt].x & 0xffffu);
+        const uint32_t dbits = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(lane_row4, static_cast<int>(own)));
+        d[rt] = static_cast<double>(f16_bits_to_float(dbits));
     }
-    const uint32_t own = (b & 1) ? (o.win.x >> 16) : (o.win.x & 0xffffu);
-    const uint32_t dbits = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(lane_row4, static_cast<int>(own)));
-    const double d = static_cast<double>(f16_bits_to_float(dbits));
 #pragma unroll
     for (int t = 0; t < AT; ++t) {
         const float xs[8] = {o.x[t][0].x, o.x[t][0].y, o.x[t][0].z, o.x[t][0].w,
                              o.x[t][1].x, o.x[t][1].y, o.x[t][1].z, o.x[t][1].w};
-        v4d p = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-            p = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(xs[s]), q[s], p, 0, 0, 0);
+        for (int rt = 0; rt < RT; ++rt) {
+            v4d p = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fma(d, p[v], acc[t][v]);
+            for (int s = 0; s < 8; ++s)
+                p = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(xs[s]), q[rt][s], p, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[rt][t][v] = __builtin_fma(d[rt], p[v], acc[rt][t][v]);
+        }
     }
 }
 
-template <int AT>
+// RT 16-row weight tiles per workgroup (each wave covers all of them),
+// AT 16-row activation tiles.
+// LDS of the waves' partial sums: 112 KiB at two weight and four activation tiles.
+constexpr size_t park_bytes(int rt, int at) { return size_t(kWaves - 1) * rt * at * 4 * 64 * sizeof(double); }
+
+template <int RT, int AT>
 __global__ __launch_bounds__(kThreads) void f64_mma_kernel(F64Args a) {
-    constexpr int D = 8 / AT;  // blocks per chunk: 64 MFMAs of work between a chunk's loads and its use
-    __shared__ double park[kWaves - 1][AT][4][64];
+    constexpr int D = 8 / (RT * AT);  // blocks per chunk: 64 MFMAs of work between a chunk's loads and its use
+    __shared__ double park[kWaves - 1][RT][AT][4][64];
+    static_assert(sizeof(park) == park_bytes(RT, AT));
     const int lane = threadIdx.x & 63;
     const int lane_row4 = (lane & 15) << 2;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t row = blockIdx.x * 16u + static_cast<uint32_t>(lane & 15);
+    const uint32_t row = blockIdx.x * (16u * RT) + static_cast<uint32_t>(lane & 15);
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.w), 0, a.w_bytes, kBufferDword3);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(a.x), 0, static_cast<uint32_t>(a.rows) * a.k * 4, kBufferDword3);
 
-    v4d acc[AT];
+    v4d acc[RT][AT];
 #pragma unroll
-    for (int t = 0; t < AT; ++t) acc[t] = v4d{0.0, 0.0, 0.0, 0.0};
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int t = 0; t < AT; ++t) acc[rt][t] = v4d{0.0, 0.0, 0.0, 0.0};
 
     // this wave's blocks: wave + kWaves j for j < mine, in chunks of D blocks
     // loaded into two register buffers in turn, each chunk's loads issued
@@ -150,69 +171,77 @@ __global__ __launch_bounds__(kThreads) void f64_mma_kernel(F64Args a) {
     const int mine = wave < nb ? (nb - wave + kWaves - 1) / kWaves : 0;
     const int last = std::max(mine - 1, 0);
     auto block_of = [&](int j) { return static_cast<uint32_t>(wave + kWaves * std::min(j, last)); };
-    Ops<AT> ping[D], pong[D];
+    Ops<RT, AT> ping[D], pong[D];
 #pragma unroll
-    for (int c = 0; c < D; ++c) load_ops<AT>(a, rw, rx, row, block_of(c), lane, c < mine, ping[c]);
+    for (int c = 0; c < D; ++c) load_ops<RT, AT>(a, rw, rx, row, block_of(c), lane, c < mine, ping[c]);
     int j0 = 0;
     for (; j0 + 2 * D < mine; j0 += 2 * D) {
 #pragma unroll
         for (int c = 0; c < D; ++c)
-            load_ops<AT>(a, rw, rx, row, block_of(j0 + D + c), lane, j0 + D + c < mine, pong[c]);
+            load_ops<RT, AT>(a, rw, rx, row, block_of(j0 + D + c), lane, j0 + D + c < mine, pong[c]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < D; ++c) math_block<AT>(ping[c], block_of(j0 + c), lane_row4, acc);
+        for (int c = 0; c < D; ++c) math_block<RT, AT>(ping[c], block_of(j0 + c), lane_row4, acc);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < D; ++c)
-            load_ops<AT>(a, rw, rx, row, block_of(j0 + 2 * D + c), lane, j0 + 2 * D + c < mine, ping[c]);
+            load_ops<RT, AT>(a, rw, rx, row, block_of(j0 + 2 * D + c), lane, j0 + 2 * D + c < mine, ping[c]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < D; ++c) math_block<AT>(pong[c], block_of(j0 + D + c), lane_row4, acc);
+        for (int c = 0; c < D; ++c) math_block<RT, AT>(pong[c], block_of(j0 + D + c), lane_row4, acc);
         __builtin_amdgcn_sched_barrier(0);
     }
     if (j0 + D < mine) {  // two chunks left: chunk j0 is in ping
 #pragma unroll
         for (int c = 0; c < D; ++c)
-            load_ops<AT>(a, rw, rx, row, block_of(j0 + D + c), lane, j0 + D + c < mine, pong[c]);
+            load_ops<RT, AT>(a, rw, rx, row, block_of(j0 + D + c), lane, j0 + D + c < mine, pong[c]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < D; ++c) math_block<AT>(ping[c], block_of(j0 + c), lane_row4, acc);
+        for (int c = 0; c < D; ++c) math_block<RT, AT>(ping[c], block_of(j0 + c), lane_row4, acc);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < D; ++c) math_block<AT>(pong[c], block_of(j0 + D + c), lane_row4, acc);
+        for (int c = 0; c < D; ++c) math_block<RT, AT>(pong[c], block_of(j0 + D + c), lane_row4, acc);
     } else if (j0 < mine) {  // one chunk left
 #pragma unroll
-        for (int c = 0; c < D; ++c) math_block<AT>(ping[c], block_of(j0 + c), lane_row4, acc);
+        for (int c = 0; c < D; ++c) math_block<RT, AT>(ping[c], block_of(j0 + c), lane_row4, acc);
     }
 
     // partial sums of waves 1..7 through LDS, added to wave 0's in wave order
     if (wave > 0) {
 #pragma unroll
-        for (int t = 0; t < AT; ++t)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) park[wave - 1][t][v][lane] = acc[t][v];
+            for (int t = 0; t < AT; ++t)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) park[wave - 1][rt][t][v][lane] = acc[rt][t][v];
     }
     __syncthreads();
     if (wave != 0 || row >= a.n) return;
 #pragma unroll
-    for (int t = 0; t < AT; ++t)
+    for (int rt = 0; rt < RT; ++rt) {
+        const uint32_t wrow = row + 16 * rt;
+        if (rt > 0 && wrow >= a.n) continue;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            double tot = acc[t][v];
+        for (int t = 0; t < AT; ++t)
 #pragma unroll
-            for (int w = 0; w < kWaves - 1; ++w) tot += park[w][t][v][lane];
-            const int r = t * 16 + (lane >> 4) + 4 * v;
-            if (r >= a.rows) continue;
-            const int64_t o = static_cast<int64_t>(r) * a.ldy + row;
-            const double res = a.residual ? static_cast<double>(a.residual[o]) : 0.0;
-            a.y[o] = static_cast<float>(tot + res);
-        }
+            for (int v = 0; v < 4; ++v) {
+                double tot = acc[rt][t][v];
+#pragma unroll
+                for (int w = 0; w < kWaves - 1; ++w) tot += park[w][rt][t][v][lane];
+                const int r = t * 16 + (lane >> 4) + 4 * v;
+                if (r >= a.rows) continue;
+                const int64_t o = static_cast<int64_t>(r) * a.ldy + wrow;
+                const double res = a.residual ? static_cast<double>(a.residual[o]) : 0.0;
+                a.y[o] = static_cast<float>(tot + res);
+            }
+    }
 }
 
-template <int AT>
+template <int RT, int AT>
 hipError_t run(const F64Args &a, hipStream_t stream) {
+    constexpr int64_t kTile = 16 * RT;
     const int64_t row_bytes = static_cast<int64_t>(a.nb) * kBlockBytes;
-    const int64_t slice = std::max<int64_t>(16, (kMaxWeightBytes / row_bytes) / 16 * 16);
+    const int64_t slice = std::max<int64_t>(kTile, (kMaxWeightBytes / row_bytes) / kTile * kTile);
     const int64_t n = a.n;
     for (int64_t r0 = 0; r0 < n; r0 += slice) {
         F64Args s = a;
@@ -221,8 +250,8 @@ hipError_t run(const F64Args &a, hipStream_t stream) {
         s.w_bytes = static_cast<uint32_t>(s.n * row_bytes);
         s.y = a.y + r0;
         s.residual = a.residual ? a.residual + r0 : nullptr;
-        const unsigned grid = (s.n + 15) / 16;
-        f64_mma_kernel<AT><<<grid, kThreads, 0, stream>>>(s);
+        const unsigned grid = static_cast<unsigned>((s.n + kTile - 1) / kTile);
+        f64_mma_kernel<RT, AT><<<grid, kThreads, 0, stream>>>(s);
         if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -248,9 +277,17 @@ hipError_t launch_f64_mma(const uint8_t *w, int64_t n, int64_t k, int rows, cons
     a.nb = static_cast<uint32_t>(k / kBlock);
     a.w_bytes = 0;
     a.rows = rows;
-    if (rows <= 16) return run<1>(a, stream);
-    if (rows <= 32) return run<2>(a, stream);
-    return run<4>(a, stream);
+    // Two weight tiles a workgroup where that takes fewer rounds of
+    // workgroups over the CUs, at about 1.65 times the time of a one-tile
+    // round: each activation load and conversion then feeds two MFMA chains.
+    const DeviceInfo dev = device_info();
+    const int64_t cus = std::max(1, dev.cus);
+    const int64_t rounds1 = (a.n + 16 * cus - 1) / (16 * cus), rounds2 = (a.n + 32 * cus - 1) / (32 * cus);
+    const bool two = 5 * rounds2 < 3 * rounds1;
+    if (rows <= 16) return two ? run<2, 1>(a, stream) : run<1, 1>(a, stream);
+    if (rows <= 32) return two ? run<2, 2>(a, stream) : run<1, 2>(a, stream);
+    if (two && park_bytes(2, 4) <= static_cast<size_t>(dev.lds_per_block)) return run<2, 4>(a, stream);
+    return run<1, 4>(a, stream);
 }
 
 }  // namespace q8

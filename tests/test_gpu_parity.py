@@ -631,9 +631,10 @@ def _big_blocks():
 @pytest.mark.parametrize("mode,rows", [("i8x2", 9), ("i8", 16), ("i8x2", 1), ("i8", 2), ("f32", 1), ("f32", 5)])
 def test_stacks_over_1gib_of_weights(mode, rows):
     """Weights of 1.06 GiB (32768x32768): every kernel family runs it as row
-    slices of at most 1 GiB, one launch each (the MFMA kernels: rows 0..30831
-    and 30832..32767; the resident GEMV: 0..30839 and 30840..32767; the tiled
-    GEMV addresses each row group from its own base).  Outputs on both sides of the slice boundaries
+    slices of at most 1 GiB, one launch each (the int8 MFMA kernels: rows
+    0..30831 and 30832..32767; the f64 MFMA kernel with two weight tiles a
+    workgroup: 0..30815 and 30816..32767; the resident GEMV: 0..30839 and
+    30840..32767; the tiled GEMV addresses each row group from its own base).  Outputs on both sides of the slice boundaries
     and at random places match the oracle one by one; in the integer modes the
     block sums of rows at the ends of the slices match it bit for bit."""
     n = k = 32768
@@ -643,8 +644,9 @@ def test_stacks_over_1gib_of_weights(mode, rows):
     x = synth.activations(rows, k, seed=3200 + rows, outlier_frac=0.01)
     wd = to_dev(blocks)
     xd = to_dev(x)
-    # slice ends: 30832 rows (int8 and f64 MFMA, multiples of 16), 30840 (GEMV)
-    edge_rows = np.array([0, 1, 30831, 30832, 30833, 30839, 30840, 30841, 32766, 32767])
+    # slice ends: 30832 rows (int8 MFMA, multiples of 16), 30816 (f64 MFMA on
+    # 32-row workgroups), 30840 (GEMV)
+    edge_rows = np.array([0, 1, 30815, 30816, 30817, 30831, 30832, 30833, 30839, 30840, 30841, 32766, 32767])
     r_idx = np.concatenate([np.repeat(np.arange(rows), edge_rows.size), rng.integers(0, rows, 512)])
     n_idx = np.concatenate([np.tile(edge_rows, rows), rng.integers(0, n, 512)])
     if mode == "f32":
@@ -670,11 +672,15 @@ def test_stacks_over_1gib_of_weights(mode, rows):
 @pytest.mark.parametrize("n,k,rows,with_res", [(14336, 4096, 64, False), (4096, 14336, 16, True),
                                                (6144, 4096, 33, False), (4096, 4096, 9, True),
                                                (14336, 4096, 8, True), (4096, 14336, 5, False),
-                                               (14336, 4096, 128, True)])
+                                               (14336, 4096, 128, True), (8180, 1024, 16, True),
+                                               (8176, 2048, 32, False), (8180, 1024, 24, True),
+                                               (8180, 1024, 64, True), (8165, 2048, 48, False)])
 def test_f32_stacks_at_full_size(n, k, rows, with_res):
     """f32 stacks of 5..64 rows (and two 64-row slices) at the workload shapes
     run on f64 MFMA tiles, every weight block read once a slice: all outputs
-    against the oracle's gate."""
+    against the oracle's gate.  Matrices of 6144 rows and more run two weight
+    tiles a workgroup; 8180, 8176 and 8165 rows end on a workgroup whose second
+    tile is partly or wholly past the matrix, or whose first tile is short."""
     say("f32 stack", n, k, rows, with_res)
     w = synth.weights(n, k, seed=2400 + rows, outlier_frac=0.01)
     x = synth.activations(rows, k, seed=2500 + rows, outlier_frac=0.005, outlier_scale=20.0)
@@ -704,14 +710,17 @@ def test_f32_stacks_with_short_k(n, k, rows):
     gate(y, r, a, f"f32 short k {n}x{k} rows={rows}")
 
 
-def test_f32_stack_rows_do_not_depend_on_the_stack():
+@pytest.mark.parametrize("n", [515, 8180])
+def test_f32_stack_rows_do_not_depend_on_the_stack(n):
     """On the f64 MFMA kernel each output is one lane's f64 total over the
     blocks, in an order fixed by k alone (block sums from chained MFMAs, then
     the waves' partials in wave order), whatever the other rows of the stack
-    hold and however many activation tiles it has: a row comes out with the
-    same bits from stacks of 5, 9, 16, 17, 33 and 64 rows and from offset
-    stacks."""
-    n, k = 515, 4096
+    hold, however many activation tiles it has and however many weight tiles
+    a workgroup takes: a row comes out with the same bits from stacks of 5, 9,
+    16, 17, 33 and 64 rows and from offset stacks.  At 8180 rows every stack
+    runs two weight tiles a workgroup; its first 515 weight rows alone run one
+    tile a workgroup and give the same bits."""
+    k = 4096
     say("f32 stack rows vs stack", n, k)
     w = synth.weights(n, k, seed=2701)
     x = synth.activations(64, k, seed=2702)
@@ -719,9 +728,13 @@ def test_f32_stack_rows_do_not_depend_on_the_stack():
     full = q8.matmul_rows("f32", wd, n, k, x=xd)
     parts = {(r0, r1): q8.matmul_rows("f32", wd, n, k, x=xd[r0:r1].contiguous())
              for r0, r1 in ((0, 5), (0, 9), (0, 16), (0, 17), (0, 33), (20, 64), (50, 64), (56, 64))}
+    head = {rows: q8.matmul_rows("f32", wd[:515].contiguous(), 515, k, x=xd[:rows].contiguous())
+            for rows in (5, 17, 64)} if n > 515 else {}
     torch.cuda.synchronize()
     for (r0, r1), y in parts.items():
         assert torch.equal(y, full[r0:r1]), (r0, r1)
+    for rows, y in head.items():
+        assert torch.equal(y, full[:rows, :515]), rows
 
 
 def test_f32_stack_inplace_residual():
