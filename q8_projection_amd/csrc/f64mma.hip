@@ -17,10 +17,10 @@
 // the numerics define the f32 mode.  Each output is rounded to f32 once, after
 // the residual is added in f64.
 //
-// Work split: one workgroup per 16-row weight tile.  Its 8 waves take the
-// blocks of k in turn (wave g: blocks g, g + 8, ...) for every activation tile
-// of the stack, so each weight block is read by one wave of one workgroup; the
-// waves' partial sums are added in wave order at the end.  Operands come from
+// Work split: one workgroup per one or two 16-row weight tiles.  Its 8 waves
+// take the blocks of k in turn (wave g: blocks g, g + 8, ...) for every weight
+// and activation tile, so each weight block is read by one wave of one
+// workgroup; the waves' partial sums are added in wave order at the end.  Operands come from
 // memory with range-checked buffer loads, a chunk of D blocks ahead of the
 // MFMAs.  Every workgroup reads the stack (through L2); HBM serves each weight
 // block one time.
@@ -135,11 +135,11 @@ __device__ __forceinline__ void math_block(const Ops<RT, AT> &o, uint32_t b, int
     }
 }
 
-// RT 16-row weight tiles per workgroup (each wave covers all of them),
-// AT 16-row activation tiles.
 // LDS of the waves' partial sums: 112 KiB at two weight and four activation tiles.
 constexpr size_t park_bytes(int rt, int at) { return size_t(kWaves - 1) * rt * at * 4 * 64 * sizeof(double); }
 
+// RT 16-row weight tiles per workgroup (each wave covers all of them),
+// AT 16-row activation tiles.
 template <int RT, int AT>
 __global__ __launch_bounds__(kThreads) void f64_mma_kernel(F64Args a) {
     constexpr int D = 8 / (RT * AT);  // blocks per chunk: 64 MFMAs of work between a chunk's loads and its use
