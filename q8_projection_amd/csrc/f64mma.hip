@@ -86,10 +86,11 @@ __device__ __forceinline__ void load_ops(const F64Args &a, __amdgpu_buffer_rsrc_
         const uint32_t dead = oob_bit(live && wrow < a.n);
         o.win[rt] = __builtin_amdgcn_raw_buffer_load_b96(rw, ((blk * kBlockBytes + 8 * kq) & ~3u) | dead, 0, 0);
     }
+    const uint32_t x0 = (r16 * a.k + b * kBlock + 8 * kq) * 4;  // tile t adds 64 t k bytes
 #pragma unroll
     for (int t = 0; t < AT; ++t) {
         const uint32_t r = static_cast<uint32_t>(t * 16) + r16;
-        const uint32_t off = ((r * a.k + b * kBlock + 8 * kq) * 4) | oob_bit(live && r < static_cast<uint32_t>(a.rows));
+        const uint32_t off = (x0 + static_cast<uint32_t>(t) * 64u * a.k) | oob_bit(live && r < static_cast<uint32_t>(a.rows));
         o.x[t][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
         o.x[t][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16, 0, 0);
     }
