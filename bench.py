@@ -508,7 +508,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed step replays before the timed ones (200 steps are ~30 ms; with 10 the timed "
+                         "steps ran about 1%% slower)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle timing on all threads (half as long again on one thread)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
