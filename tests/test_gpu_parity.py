@@ -678,9 +678,11 @@ def test_stacks_over_1gib_of_weights(mode, rows):
 def test_f32_stacks_at_full_size(n, k, rows, with_res):
     """f32 stacks of 5..64 rows (and two 64-row slices) at the workload shapes
     run on f64 MFMA tiles, every weight block read once a slice: all outputs
-    against the oracle's gate.  Matrices of 6144 rows and more run two weight
-    tiles a workgroup; 8180, 8176 and 8165 rows end on a workgroup whose second
-    tile is partly or wholly past the matrix, or whose first tile is short."""
+    against the oracle's gate.  A workgroup takes two weight tiles where that
+    cuts the rounds of workgroups over the CUs enough: on 256 CUs the 6144-,
+    8165..8180- and 14336-row cases here, not the 4096-row ones.  8180, 8176
+    and 8165 rows end on a workgroup whose second tile is partly or wholly past
+    the matrix, or whose first tile is short."""
     say("f32 stack", n, k, rows, with_res)
     w = synth.weights(n, k, seed=2400 + rows, outlier_frac=0.01)
     x = synth.activations(rows, k, seed=2500 + rows, outlier_frac=0.005, outlier_scale=20.0)
