@@ -739,8 +739,11 @@ def test_f32_stack_rows_do_not_depend_on_the_stack(n):
         assert torch.equal(y, full[:rows, :515]), rows
 
 
-def test_f32_stack_inplace_residual():
-    n, k, rows = 1000, 2048, 20
+@pytest.mark.parametrize("n,rows", [(1000, 20), (8180, 40)])
+def test_f32_stack_inplace_residual(n, rows):
+    """y may be the residual buffer itself, with one or two weight tiles a
+    workgroup (8180 rows take two)."""
+    k = 2048
     say("f32 stack in-place residual", n, k, rows)
     w = synth.weights(n, k, seed=2801)
     x = synth.activations(rows, k, seed=2802)
