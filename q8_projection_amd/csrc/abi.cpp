@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "../../include/q8.h"
 #include "launch.h"
@@ -102,21 +103,27 @@ bool mma_serves(int mode, int64_t n, int64_t k, int rows, const void *w, const i
 
 namespace q8 {
 
+// Per-device attributes, queried once.  The cache entry packs both values in
+// one atomic word, so concurrent first calls from several host threads each
+// store the same value and no caller sees one field without the other.
 DeviceInfo device_info() {
-    static DeviceInfo cache[kMaxDevices];
+    static std::atomic<uint64_t> cache[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-    DeviceInfo &c = cache[dev];
-    if (c.cus == 0) {
+    uint64_t v = cache[dev].load(std::memory_order_acquire);
+    if (v == 0) {
         int cus = 0, lds = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
         if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || lds <= 0)
             lds = 64 * 1024;
-        c.lds_per_block = lds;
-        c.cus = cus;
+        v = (static_cast<uint64_t>(static_cast<uint32_t>(lds)) << 32) | static_cast<uint32_t>(cus);
+        cache[dev].store(v, std::memory_order_release);
     }
-    return c;
+    DeviceInfo d;
+    d.cus = static_cast<int>(static_cast<uint32_t>(v));
+    d.lds_per_block = static_cast<int>(v >> 32);
+    return d;
 }
 
 }  // namespace q8
