@@ -276,7 +276,7 @@ def test_stack_rows_equal_single_rows():
 
 @pytest.mark.parametrize("mode", ["i8", "i8x2"])
 @pytest.mark.parametrize("n,k,rows", [(5000, 2048, 1), (4096, 14336, 1), (700, 1088, 1), (1000, 4096, 3),
-                                      (999, 2048, 8), (300, 512, 8)])
+                                      (999, 2048, 8), (300, 512, 8), (4096, 4096, 1), (600, 8192, 8)])
 def test_quantization_inside_the_projection_is_bitwise_the_same(mode, n, k, rows):
     """An integer-mode stack given as f32 x is quantized inside the projection
     (fused into its consumer) with the same bits as q8_quantize_act followed by
