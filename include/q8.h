@@ -152,6 +152,48 @@ q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t 
                          const int8_t *lo, const float *scale, const float *x, const float *residual,
                          float *y, void *stream);
 
+/* q8_matmul_rows with a caller workspace that lets short integer stacks split
+ * K across workgroups: the batched decode step's projections (model::author
+ * page, Functions: decode_batch) on a matrix of at most 16 rows per CU with a
+ * long K.  There q8_matmul_rows gives every workgroup one 16-row tile and the
+ * whole stack; this call gives each 64-row range's K to 2, 4 or 8 workgroups,
+ * which copy 1/2 .. 1/8 of the stack each.  Their f64 partial sums meet in the
+ * workspace and the last workgroup of a range to finish (told by an atomic
+ * counter) adds them in split order, so the result does not depend on the
+ * order of arrival; its f64 sums are added in another order than
+ * q8_matmul_rows's, so the two may differ in the last bits of an output.  The
+ * combine costs about 2 us, so only stacks of at least 400 KB split (rows x k
+ * bytes, twice that in Q8_ACT_I8X2): 8 two-word rows from k = 25600 on (on
+ * 4096 x 28672 measured 27.6 against 29.5-32 us unsplit).
+ * Arguments as q8_matmul_rows, plus:
+ *   workspace       : device memory, 16-byte aligned, of at least
+ *                     q8_matmul_rows_workspace_bytes(mode, n, k, rows) bytes,
+ *                     zero-filled by the caller before its first use.  It
+ *                     starts with 32-bit counters, one for each 64-row range
+ *                     the tallest matrix that splits can have on this device
+ *                     (16 rows per CU), which every call leaves at zero again;
+ *                     the rest is scratch.  So one workspace, as large as the
+ *                     largest call's, serves call after call of any shape
+ *                     without clearing, but two calls in flight at once must
+ *                     not share it.
+ *   workspace_bytes : its size in bytes.
+ * Where q8_matmul_rows_workspace_bytes is 0 (f32 mode, one row or more than
+ * one activation tile: over 8 two-word or 16 one-word rows, more than 16 rows
+ * per CU, a stack under 400 KB, k not a multiple of 256, weights of 1 GiB or
+ * more), for a stack given as x, and for stacks q8_matmul_rows would not run
+ * on its MFMA kernels (16-byte alignment), the call is q8_matmul_rows's and the
+ * workspace is not read or written (it may be NULL).
+ * Errors: as q8_matmul_rows; with a workspace needed: Q8_E_NULL (none given),
+ * Q8_E_ALIGN, Q8_E_SHAPE (workspace_bytes too small), Q8_E_ALIAS (workspace
+ * overlapping an input or y). */
+q8_status q8_matmul_rows_ws(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
+                            const int8_t *lo, const float *scale, const float *x, const float *residual,
+                            float *y, void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Bytes of the q8_matmul_rows_ws workspace for this call on the current device,
+ * 0 where the call does not split K (or the arguments are out of range). */
+int64_t q8_matmul_rows_workspace_bytes(int mode, int64_t n, int64_t k, int64_t rows);
+
 /* y = W x (+ residual) for one activation row, and idx = argmax_i y[i] (the
  * lowest i among equal maxima) from the same launch: the LM head closing a
  * decode step (model::author page, Functions: the head reads the last row

@@ -36,6 +36,8 @@ SIGNATURES = {
     "q8_quantize_act": (_I, [_I, _P, _I64, _I64, _P, _P, _P, _P]),
     "q8_matvec": (_I, [_I, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "q8_matmul_rows": (_I, [_I, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "q8_matmul_rows_ws": (_I, [_I, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I64, _P]),
+    "q8_matmul_rows_workspace_bytes": (_I64, [_I, _I64, _I64, _I64]),
     "q8_matvec_argmax": (_I, [_I, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "q8_argmax_workspace_bytes": (_I64, [_I64]),
     "q8_matvec_argmax_noalloc": (_I, [_I, _P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -191,6 +193,40 @@ def matmul_rows(mode, w: torch.Tensor, n: int, k: int, hi=None, lo=None, scale=N
     _want(out, "out", torch.float32, rows * n)
     _check("q8_matmul_rows", lib().q8_matmul_rows(m, _ptr(w), n, k, rows, _ptr(hi), _ptr(lo), _ptr(scale),
                                                   _ptr(x), _ptr(residual), _ptr(out), _stream(stream)))
+    return out
+
+
+def matmul_rows_workspace_bytes(mode, n: int, k: int, rows: int) -> int:
+    """Bytes of the matmul_rows_ws workspace for this call (0: it does not split K)."""
+    return int(lib().q8_matmul_rows_workspace_bytes(_mode(mode), n, k, rows))
+
+
+def matmul_rows_ws(mode, w: torch.Tensor, n: int, k: int, hi=None, lo=None, scale=None, x=None,
+                   residual=None, out=None, workspace=None, rows: int | None = None, stream=None) -> torch.Tensor:
+    """matmul_rows with K split across workgroups for short integer stacks on
+    short matrices (q8_matmul_rows_ws).  The workspace (uint8, at least
+    matmul_rows_workspace_bytes) must start zero-filled; each call leaves its
+    counters at zero, so a caller may keep one per stream and pass it every
+    time.  None allocates a zero-filled one for this call."""
+    m = _mode(mode)
+    src = x if (m == 0 or hi is None) else hi
+    if rows is None:
+        rows = 1 if src is None or src.dim() == 1 else src.shape[0]
+    dev = _device_of(w, src)
+    if out is None:
+        out = torch.empty((rows, n), dtype=torch.float32, device=dev)
+    need = matmul_rows_workspace_bytes(mode, n, k, rows)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+    _want_weights(w, n, k)
+    _want_stack(m, rows, k, hi, lo, scale, x)
+    _want(residual, "residual", torch.float32, rows * n, optional=True)
+    _want(out, "out", torch.float32, rows * n)
+    _want(workspace, "workspace", torch.uint8, need, optional=True)
+    wsb = 0 if workspace is None else workspace.numel()
+    _check("q8_matmul_rows_ws", lib().q8_matmul_rows_ws(m, _ptr(w), n, k, rows, _ptr(hi), _ptr(lo), _ptr(scale),
+                                                        _ptr(x), _ptr(residual), _ptr(out), _ptr(workspace), wsb,
+                                                        _stream(stream)))
     return out
 
 

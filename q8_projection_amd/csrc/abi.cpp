@@ -210,6 +210,41 @@ q8_status q8_matvec(int mode, const void *w, int64_t n, int64_t k, const int8_t 
     return q8_matmul_rows(mode, w, n, k, 1, hi, lo, scale, x, residual, y, stream);
 }
 
+int64_t q8_matmul_rows_workspace_bytes(int mode, int64_t n, int64_t k, int64_t rows) {
+    if (mode != Q8_ACT_I8 && mode != Q8_ACT_I8X2) return 0;
+    if (check_sizes(n, k, rows) != Q8_OK || n < 1 || rows < 2 || rows > 64) return 0;
+    return q8::mma_ksplit_bytes(mode, n, k, static_cast<int>(rows));
+}
+
+q8_status q8_matmul_rows_ws(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
+                            const int8_t *lo, const float *scale, const float *x, const float *residual, float *y,
+                            void *workspace, int64_t workspace_bytes, void *stream) {
+    if (q8_status s = check_sizes(n, k, rows); s != Q8_OK) return s;  // before rows * n is formed
+    if (q8_status s = check_projection(mode, w, n, k, rows, hi, lo, scale, x, residual, y, rows * n * 4, true, true);
+        s != Q8_OK)
+        return s;
+    const int64_t need = q8_matmul_rows_workspace_bytes(mode, n, k, rows);
+    const bool inside = mode != Q8_ACT_F32 && !hi;
+    // stacks this call does not split: q8_matmul_rows, the workspace untouched
+    if (need == 0 || inside)
+        return q8_matmul_rows(mode, w, n, k, rows, hi, lo, scale, x, residual, y, stream);
+    if (!workspace) return Q8_E_NULL;
+    if (!aligned(workspace, 16)) return Q8_E_ALIGN;
+    if (workspace_bytes < need) return Q8_E_SHAPE;
+    const int64_t nb = k / 32;
+    const void *ins[] = {w, hi, lo, scale, residual, y};
+    const int64_t in_bytes[] = {n * nb * 34, rows * k, mode == Q8_ACT_I8X2 ? rows * k : 0, rows * nb * 4,
+                                residual ? rows * n * 4 : 0, rows * n * 4};
+    for (int i = 0; i < 6; ++i)
+        if (ins[i] && in_bytes[i] > 0 && overlap(workspace, need, ins[i], in_bytes[i])) return Q8_E_ALIAS;
+    const int r = static_cast<int>(rows);
+    if (!mma_serves(mode, n, k, r, w, hi, lo, scale, false))
+        return q8_matmul_rows(mode, w, n, k, rows, hi, lo, scale, x, residual, y, stream);
+    return from_hip(q8::launch_mma_ksplit(mode, static_cast<const uint8_t *>(w), n, k, r, hi,
+                                          mode == Q8_ACT_I8X2 ? lo : nullptr, scale, residual, y, workspace,
+                                          as_stream(stream)));
+}
+
 int64_t q8_argmax_workspace_bytes(int64_t n) {
     if (n < 1 || n > INT32_MAX) return 0;
     return 16 + 8 * q8::gemv_row_grid(n);

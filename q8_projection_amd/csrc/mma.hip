@@ -32,4 +32,16 @@ hipError_t launch_mma(int mode, const uint8_t *w, int64_t n, int64_t k, int rows
     return launch_mma_impl<false>(mode, w, n, k, rows, hi, lo, scale, residual, y, ldy, nullptr, stream);
 }
 
+int64_t mma_ksplit_bytes(int mode, int64_t n, int64_t k, int rows) {
+    if (rows < 2) return 0;
+    const KsPlan p = ks_plan(mode, n, k, rows);
+    return p.ksplit > 1 ? p.bytes : 0;
+}
+
+hipError_t launch_mma_ksplit(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
+                             const int8_t *lo, const float *scale, const float *residual, float *y, void *workspace,
+                             hipStream_t stream) {
+    return launch_mma_ksplit_impl(mode, w, n, k, rows, hi, lo, scale, residual, y, n, workspace, stream);
+}
+
 }  // namespace q8

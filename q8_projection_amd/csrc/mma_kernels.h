@@ -130,6 +130,12 @@ struct MmaArgs {
     int32_t *sums;           // block-sum export [rows][sums_ld][nb][sums_words], or null
     int64_t sums_ld;         // weight rows of the whole call (the export's row stride)
     int sums_words;          // 2 for a two-word stack, else 1
+    // K split over workgroups (ksplit > 1): workgroup g takes row range
+    // g / ksplit and chunks [nchunks * (g % ksplit), + nchunks); the ranges'
+    // partial sums meet in a caller workspace (ks_part, ks_count: below).
+    int ksplit;
+    double *ks_part;         // [ranges][ksplit][RT * TT * kVals * 64] f64 partials
+    uint32_t *ks_count;      // [ranges] arrivals, zero between calls
 };
 
 struct Rsrcs {
@@ -206,14 +212,15 @@ __device__ __forceinline__ uint32_t plan_copy(const MmaArgs &a, int i, int lane,
     return kOob;
 }
 
-// Copies of chunk c into the slot at LDS address `slot`: copy i is issued by
+// Copies of chunk kc0 + c into the slot at LDS address `slot` (chunk c of the
+// workgroup's K range; c >= nchunks reads nothing): copy i is issued by
 // wave i % W, so a wave issues kPerWave or kPerWaveLow copies per chunk, the
 // same number for every chunk (chunks past the end read nothing), and its
 // vmcnt waits are exact.
 template <int RT, int TT, int WORDS, int GR, int GA, int GB>
 __device__ __forceinline__ void issue_chunk(const Rsrcs &rs,
                                             const uint32_t (&base)[Layout<RT, TT, WORDS, GR, GA, GB>::kPerWave],
-                                            uint32_t slot, int c, int nchunks, int wave) {
+                                            uint32_t slot, int c, int nchunks, int wave, int kc0) {
     using L = Layout<RT, TT, WORDS, GR, GA, GB>;
     constexpr int W = L::W;
     const uint32_t chunk_oob = c < nchunks ? 0u : kOob;
@@ -223,15 +230,15 @@ __device__ __forceinline__ void issue_chunk(const Rsrcs &rs,
         if (i >= L::kCopies) {
             // not this wave's: the copies are dealt round-robin
         } else if (i < L::kWCopies) {
-            copy16(rs.w, slot + i * kCopyBytes, (base[u] + c * kRowChunk) | chunk_oob);
+            copy16(rs.w, slot + i * kCopyBytes, (base[u] + (kc0 + c) * kRowChunk) | chunk_oob);
         } else if (i < L::kWCopies + L::kACopies) {
             // slots 0..7 hold hi rows, 8..15 lo rows; a copy fills kColsPerCopy of them
             const bool lo = WORDS == 2 && ((i - L::kWCopies) % kTileCopies) * kColsPerCopy >= 8;
             copy16(lo ? rs.lo : rs.hi, slot + i * kCopyBytes,
-                   (base[u] + c * kActChunk) | chunk_oob | (lo ? rs.lo_oob : 0u));
+                   (base[u] + (kc0 + c) * kActChunk) | chunk_oob | (lo ? rs.lo_oob : 0u));
         } else {
             copy4(rs.s, slot + L::kSOff + (i - L::kWCopies - L::kACopies) * 256,
-                  (base[u] + c * (kChunkBlocks * 4)) | chunk_oob);
+                  (base[u] + (kc0 + c) * (kChunkBlocks * 4)) | chunk_oob);
         }
     }
 }
@@ -401,7 +408,13 @@ __global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_kernel(MmaArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     constexpr int RTW = L::kRTW;
     const int ga = wave % GA, gr = (wave / GA) % GR, gb = wave / (GA * GR);
-    const uint32_t r0 = blockIdx.x * static_cast<uint32_t>(a.rows_per_wg);
+    // K split serves stacks of one activation tile only; other layouts compile without it
+    constexpr bool kCanSplit = !SUMS && TT == 1;
+    const int ksplit = kCanSplit ? a.ksplit : 1;
+    const uint32_t range = blockIdx.x / static_cast<uint32_t>(ksplit);
+    const int split = static_cast<int>(blockIdx.x - range * static_cast<uint32_t>(ksplit));
+    const int kc0 = split * a.nchunks;  // this workgroup's first chunk
+    const uint32_t r0 = range * static_cast<uint32_t>(a.rows_per_wg);
     const int rcount = static_cast<int>(min(static_cast<uint32_t>(a.rows_per_wg), a.n - r0));
 
     Rsrcs rs;
@@ -447,7 +460,7 @@ __global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_kernel(MmaArgs a) {
 #pragma unroll
     for (int c = 0; c < L::kDepth - 1; ++c) {
         if (c == 1) __builtin_amdgcn_s_sleep(20);  // 20 x 64 clocks
-        issue_chunk<RT, TT, WORDS, GR, GA, GB>(rs, plan, base + c * L::kSlotBytes, c, a.nchunks, wave);
+        issue_chunk<RT, TT, WORDS, GR, GA, GB>(rs, plan, base + c * L::kSlotBytes, c, a.nchunks, wave, kc0);
     }
 
     const bool more = wave < L::kCopies % W;  // this wave issues kPerWave copies per chunk, else kPerWaveLow
@@ -461,9 +474,10 @@ __global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_kernel(MmaArgs a) {
             wait_copies<L::kPerWaveLow * (L::kDepth - 2)>();
         ring_barrier();  // everyone's have; slot nxt is free
         issue_chunk<RT, TT, WORDS, GR, GA, GB>(rs, plan, base + nxt * L::kSlotBytes, c + L::kDepth - 1, a.nchunks,
-                                           wave);
+                                           wave, kc0);
         const uint8_t *slot = smem + cur * L::kSlotBytes;
-        compute_blocks<RT, TT, WORDS, GR, GA, GB, L::kBlocksPerWave, SUMS>(slot, offs, acc, a, sl, c * kChunkBlocks);
+        compute_blocks<RT, TT, WORDS, GR, GA, GB, L::kBlocksPerWave, SUMS>(slot, offs, acc, a, sl,
+                                                                           (kc0 + c) * kChunkBlocks);
         // the export's stores have completed before later waits count copies
         if constexpr (SUMS) wait_copies<0>();
         cur = cur + 1 == L::kDepth ? 0 : cur + 1;
@@ -502,6 +516,62 @@ __global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_kernel(MmaArgs a) {
         }
         ring_barrier();
     }
+    // K split: these totals are one of ksplit partials of the row range.  Each
+    // goes to the workspace as agent-scope atomic stores (written through this
+    // XCD's L2 to the device-coherent level; no L2-wide write-back), completed
+    // before the workgroup counts itself in.  The workgroup that counts last
+    // reads the others' partials at agent scope, adds all of them in split
+    // order (the same bits whichever workgroup is last), writes the outputs as
+    // the unsplit kernel does, and returns the counter to zero.
+    if (kCanSplit && ksplit > 1) {
+        __shared__ int ks_last;
+        constexpr int kTot = RT * TT * L::kVals * 64;
+        const size_t range_part = static_cast<size_t>(range) * ksplit * kTot;
+        if (gb == 0) {
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                for (int t = 0; t < AT; ++t)
+#pragma unroll
+                    for (int v = 0; v < L::kVals; ++v) {
+                        const int idx = (((gr * RTW + rt) * TT + ga * AT + t) * L::kVals + v) * 64 + lane;
+                        __hip_atomic_store(a.ks_part + range_part + static_cast<size_t>(split) * kTot + idx,
+                                           acc[rt][t][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __syncthreads();  // every partial of this workgroup has completed
+        if (threadIdx.x == 0) {
+            const uint32_t done = __hip_atomic_fetch_add(a.ks_count + range, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            ks_last = done == static_cast<uint32_t>(ksplit - 1);
+        }
+        __syncthreads();
+        if (!ks_last) return;
+        if (gb == 0) {
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                for (int t = 0; t < AT; ++t)
+#pragma unroll
+                    for (int v = 0; v < L::kVals; ++v) {
+                        const int idx = (((gr * RTW + rt) * TT + ga * AT + t) * L::kVals + v) * 64 + lane;
+                        double tot = 0.0;
+                        for (int s2 = 0; s2 < ksplit; ++s2) {
+                            const double p = s2 == split
+                                                 ? acc[rt][t][v]
+                                                 : __hip_atomic_load(a.ks_part + range_part +
+                                                                         static_cast<size_t>(s2) * kTot + idx,
+                                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            tot = s2 == 0 ? p : tot + p;
+                        }
+                        acc[rt][t][v] = tot;
+                    }
+        }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(a.ks_count + range, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
     // The waves of block group 0 hold the totals of their tiles; park them as
     // [rt][tile][v][lane] and let every wave write a share of the outputs.
     if (gb == 0) {
@@ -603,7 +673,7 @@ __global__ __launch_bounds__(64 * W, 1) void mma_wave_kernel(MmaArgs a) {
     const int mine = wave < a.nchunks ? (a.nchunks - wave + W - 1) / W : 0;
 #pragma unroll
     for (int p = 0; p < P; ++p)
-        issue_chunk<1, 1, WORDS, 1, 1, 1>(rs, plan, ring_lds + p * L::kSlotBytes, wave + W * p, a.nchunks, 0);
+        issue_chunk<1, 1, WORDS, 1, 1, 1>(rs, plan, ring_lds + p * L::kSlotBytes, wave + W * p, a.nchunks, 0, 0);
     int slot = 0;
     for (int i = 0; i < mine; ++i) {
         wait_copies<(P - 1) * L::kCopies>();  // chunk i's copies have landed
@@ -613,7 +683,7 @@ __global__ __launch_bounds__(64 * W, 1) void mma_wave_kernel(MmaArgs a) {
         if constexpr (SUMS) wait_copies<0>();
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot is read before it is refilled
         issue_chunk<1, 1, WORDS, 1, 1, 1>(rs, plan, ring_lds + slot * L::kSlotBytes, wave + W * (i + P), a.nchunks,
-                                          0);
+                                          0, 0);
         slot = slot + 1 == P ? 0 : slot + 1;
     }
     wait_copies<0>();  // the trailing copies read nothing but still write the ring
@@ -655,7 +725,7 @@ template <int RT, int TT, int WORDS, int GR, int GA, int GB, bool SUMS>
 hipError_t run(const MmaArgs &a, hipStream_t stream) {
     using L = Layout<RT, TT, WORDS, GR, GA, GB>;
     if (L::kLdsBytes > device_info().lds_per_block) return hipErrorInvalidConfiguration;
-    const uint32_t grid = (a.n + a.rows_per_wg - 1) / a.rows_per_wg;
+    const uint32_t grid = (a.n + a.rows_per_wg - 1) / a.rows_per_wg * static_cast<uint32_t>(a.ksplit);
     hipLaunchKernelGGL((mma_kernel<RT, TT, WORDS, GR, GA, GB, SUMS>), dim3(grid), dim3(64 * L::W), L::kLdsBytes,
                        stream, a);
     return hipGetLastError();
@@ -747,6 +817,9 @@ hipError_t launch_mma_slice(int mode, const uint8_t *w, int64_t n, int64_t k, in
     a.sums = sums;
     a.sums_ld = sums_ld;
     a.sums_words = mode == 2 ? 2 : 1;
+    a.ksplit = 1;
+    a.ks_part = nullptr;
+    a.ks_count = nullptr;
     if (at == 1 && rt <= kWaveMaxRt) {
         if (words == 2) return run_wave<2, kWaveWaves, kWaveDepth, SUMS>(a, stream);
         return run_wave<1, kWaveWaves, kWaveDepth, SUMS>(a, stream);
@@ -786,6 +859,99 @@ hipError_t launch_mma_impl(int mode, const uint8_t *w, int64_t n, int64_t k, int
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// ------------------------------------------- K split over workgroups (workspace)
+//
+// A stack of one activation tile on a matrix of at most 16 rows per CU gets
+// one 16-row tile a workgroup from the dispatch above (the wave-private
+// kernel), so every workgroup copies the whole stack: as many bytes as its
+// weights.  With a caller workspace the same stack runs instead on the shared
+// ring with 64-row ranges and K split over ksplit workgroups per range
+// (ranges x ksplit about the CU count): each workgroup copies 1/ksplit of the
+// stack.  The combine costs the last workgroup of a range three memory round
+// trips in a row (its partial written through, the counter, the others'
+// partials read), about 2 us, so the split pays only where the stack a
+// workgroup would copy unsplit is large.  Measured (8 two-word rows, 4096 x k):
+// even at k = 16384-20480 (262-328 KB of stack), 0.7 us slower at 14336, 2 us
+// faster at 28672 (459 KB) and 6 us at 57344; two rows at 28672 (115 KB) 0.9
+// us slower; 1024-2048 rows, which leave CUs idle unsplit, 5 us faster at
+// 28672.  Hence the 400 KB floor below.
+//
+// The ranges' partials meet in the workspace: one u32 counter for each range
+// the largest such matrix can have (16 CUs' rows / 64, rounded up to 16
+// bytes), then f64 partials [ranges][ksplit][4 * kVals * 64].  The counters sit
+// where no call's partials go, so one workspace serves calls of any shape.
+
+constexpr int64_t kSplitMinStackBytes = 400 * 1024;  // rows x words x k of a stack that splits
+
+struct KsPlan {
+    int words = 0;
+    int ksplit = 1;          // 1: no split for this stack
+    int64_t ranges = 0;
+    int64_t count_bytes = 0;
+    int64_t bytes = 0;
+};
+
+KsPlan ks_plan(int mode, int64_t n, int64_t k, int rows) {
+    KsPlan p;
+    if ((mode != 1 && mode != 2) || n < 1 || rows < 1) return p;
+    const bool as_two_word = mode == 1 && rows <= 8;
+    const int words = mode == 2 || as_two_word ? 2 : 1;
+    const int64_t nb = k / kBlock;
+    const int64_t cus = std::max(1, device_info().cus);
+    if (act_tiles(words, rows) != 1 || n > 16 * cus || nb % kChunkBlocks != 0) return p;
+    if (n * nb * kBlockBytes >= kMaxMmaWeightBytes) return p;
+    if (int64_t(rows) * (mode == 2 ? 2 : 1) * k < kSplitMinStackBytes) return p;
+    const int64_t ranges = (n + 63) / 64;
+    int split = 1;
+    for (int c : {8, 4, 2})
+        if (ranges * c <= cus && nb % (kChunkBlocks * c) == 0) {
+            split = c;
+            break;
+        }
+    if (split == 1) return p;
+    const int64_t tot = 4 * (words == 2 ? 2 : 4) * 64;  // RT * TT * kVals * 64 of Layout<4, 1, words, 4, 1, 4>
+    p.words = words;
+    p.ksplit = split;
+    p.ranges = ranges;
+    p.count_bytes = ((16 * cus + 63) / 64 * 4 + 15) / 16 * 16;
+    p.bytes = p.count_bytes + ranges * split * tot * 8;
+    return p;
+}
+
+hipError_t launch_mma_ksplit_impl(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
+                                  const int8_t *lo, const float *scale, const float *residual, float *y,
+                                  int64_t ldy, void *workspace, hipStream_t stream) {
+    const KsPlan p = ks_plan(mode, n, k, rows);
+    if (p.ksplit <= 1 || !workspace) return hipErrorInvalidValue;
+    const bool as_two_word = p.words == 2 && mode == 1;
+    const int64_t nb = k / kBlock;
+    MmaArgs a;
+    a.w = w;
+    a.hi = hi;
+    a.lo = as_two_word ? hi : lo;
+    a.lo_oob = as_two_word ? kOob : 0u;
+    a.scale = scale;
+    a.residual = residual;
+    a.y = y;
+    a.ldy = ldy;
+    a.n = static_cast<uint32_t>(n);
+    a.k = static_cast<uint32_t>(k);
+    a.nb = static_cast<uint32_t>(nb);
+    a.row_bytes = static_cast<uint32_t>(nb * kBlockBytes);
+    a.w_bytes = static_cast<uint32_t>(n * nb * kBlockBytes);
+    a.rows = rows;
+    a.rows_per_wg = 64;
+    a.nchunks = static_cast<int>(nb / kChunkBlocks / p.ksplit);
+    a.sums = nullptr;
+    a.sums_ld = n;
+    a.sums_words = mode == 2 ? 2 : 1;
+    a.ksplit = p.ksplit;
+    a.ks_count = static_cast<uint32_t *>(workspace);
+    a.ks_part = reinterpret_cast<double *>(static_cast<uint8_t *>(workspace) + p.count_bytes);
+    if (p.words == 2) return run_split<2, 1, 4, false>(a, stream);
+    return run_split<1, 1, 4, false>(a, stream);
 }
 
 }  // namespace

@@ -32,6 +32,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["q8_quantize_weights", "q8_quantize_act", "q8_matvec", "q8_matmul_rows",
+                            "q8_matmul_rows_ws", "q8_matmul_rows_workspace_bytes",
                             "q8_matvec_argmax", "q8_argmax_workspace_bytes", "q8_matvec_argmax_noalloc",
                             "q8_block_sums",
                             "q8_status_name", "q8_version"])
@@ -152,6 +153,60 @@ def test_aliasing():
 def _ma(mode=1, w=BASE, n=64, k=256, hi=BASE + 16 * MB, lo=BASE + 32 * MB, scale=BASE + 48 * MB, x=None,
         residual=None, y=BASE + 64 * MB, idx=BASE + 72 * MB, work=BASE + 76 * MB):
     return q8.lib().q8_matvec_argmax(mode, w, n, k, hi, lo, scale, x, residual, y, idx, work, None)
+
+
+def test_split_workspace_size():
+    """Workspace of the K-split projection: 32-bit counters for the 64-row
+    ranges of the tallest matrix that splits (16 rows per CU: 64 counters, 256
+    bytes, on a 256-CU device), then the f64 partials of every split of every
+    range: 4 tiles of 16 weight rows by the activation tile's rows (8 two-word,
+    16 one-word).  The device count of CUs is 256 here (MI355X, and the value
+    assumed with no device)."""
+    f = q8.lib().q8_matmul_rows_workspace_bytes
+    # 4096 x 28672, 8 two-word rows: 64 ranges, K in 4 parts (64 x 8 > 256 CUs)
+    assert f(2, 4096, 28672, 8) == 256 + 64 * 4 * (4 * 16 * 8) * 8
+    # 16 one-word rows: one tile of 16 one-word rows
+    assert f(1, 4096, 28672, 16) == 256 + 64 * 4 * (4 * 16 * 16) * 8
+    # one-word rows up to 8 run in the two-word layout; 8 x 57344 bytes of stack
+    assert f(1, 4096, 57344, 8) == f(2, 4096, 28672, 8)
+    # 1000 rows: 16 ranges, K in 8 parts (nb = 896 is a multiple of 64)
+    assert f(2, 1000, 28672, 8) == 256 + 16 * 8 * (4 * 16 * 8) * 8
+    # the smallest stacks that split: 400 KB (rows x k, twice in two-word mode)
+    assert f(2, 4096, 25600, 8) > 0 and f(2, 4096, 25344, 8) == 0
+    assert f(1, 4096, 25600, 16) > 0 and f(1, 4096, 25344, 16) == 0
+    # no split: f32 mode, one row, more than one activation tile, tall matrix,
+    # a stack under 400 KB (the 4096 x 14336 down projection at 8 rows: 229 KB),
+    # k not a multiple of 256, bad sizes
+    for args in ((0, 4096, 28672, 8), (2, 4096, 28672, 1), (2, 4096, 28672, 9), (1, 4096, 28672, 17),
+                 (2, 14336, 28672, 8), (2, 4096, 14336, 8), (1, 4096, 28672, 8), (2, 4096, 28672 - 64, 8),
+                 (2, 0, 28672, 8), (2, 4096, 28672, 0), (2, -1, 28672, 8), (2, 4096, 100, 8),
+                 (7, 4096, 28672, 8)):
+        assert f(*args) == 0, args
+
+
+def _mws(mode=2, w=BASE, n=4096, k=28672, rows=8, hi=BASE + 128 * MB, lo=BASE + 129 * MB,
+         scale=BASE + 130 * MB, x=None, residual=None, y=BASE + 131 * MB, work=BASE + 132 * MB, work_bytes=2 * MB):
+    return q8.lib().q8_matmul_rows_ws(mode, w, n, k, rows, hi, lo, scale, x, residual, y, work, work_bytes, None)
+
+
+def test_split_projection_validation():
+    """4096 x 28672 with 8 two-word rows: weights 119 MiB from BASE, hi, lo,
+    scales and y 1 MiB apart above them, the workspace at +132 MiB."""
+    need = q8.lib().q8_matmul_rows_workspace_bytes(2, 4096, 28672, 8)
+    assert need > 0
+    assert _mws(work=None) == NULL
+    assert _mws(work=BASE + 132 * MB + 8) == ALIGN
+    assert _mws(work_bytes=need - 1) == SHAPE
+    assert _mws(work=BASE + 131 * MB + 64 * 1024) == ALIAS        # inside y
+    assert _mws(work=BASE + 100 * MB) == ALIAS                    # inside the weights
+    assert _mws(work=BASE + 130 * MB + 4096) == ALIAS             # inside the scales
+    assert _mws(residual=BASE + 132 * MB + 4096) == ALIAS         # residual inside the workspace
+    # the projection's own checks come first
+    assert _mws(mode=5) == MODE
+    assert _mws(k=100) == SHAPE
+    assert _mws(hi=None) == NULL
+    assert _mws(y=BASE + 131 * MB + 2) == ALIGN
+    assert _mws(y=BASE + 128 * MB + 4096) == ALIAS                # y over hi
 
 
 def test_argmax_workspace_size():

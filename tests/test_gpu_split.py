@@ -1,0 +1,222 @@
+"""The K-split projection (q8_matmul_rows_ws) against the CPU oracle, on the GPU.
+
+A short integer stack on a matrix of at most 16 rows per CU (a batched decode
+step's down projection, model::author page, Functions: decode_batch) is split
+over workgroups along K; the partial sums of a 64-row range meet in a caller
+workspace and the last workgroup to arrive adds them in split order.  Checked
+here: the gate against the oracle at full size and on ragged and tiny shapes,
+bitwise equal results from call to call (the order of arrival does not show),
+counters left at zero, in-place residual, one workspace shared by calls of
+different shapes, graph replays, and the calls that do not split (which are
+q8_matmul_rows's, bit for bit)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import q8_projection_amd as q8
+import synth
+from helpers import gate, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    torch.cuda.set_device(0)
+    q8.lib()
+    yield
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _case(n, k, rows, mode, with_res, seed):
+    blocks = oracle.quantize_weights(synth.weights(n, k, seed=seed))
+    x = synth.activations(rows, k, seed=seed + 1)
+    res = synth.normal(seed + 2, (rows, n)) if with_res else None
+    return blocks, x, res
+
+
+def _expected(mode, blocks, n, k, x, res):
+    hi, lo, sc = oracle.quantize_act(mode, x)
+    return oracle.project(mode, blocks, n, k, x.shape[0], hi=hi, lo=lo, scale=sc, residual=res)
+
+
+def _counters_zero(ws, n):
+    """The counters of every range a splitting matrix can have (16 rows per CU)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    count_bytes = ((16 * cus + 63) // 64 * 4 + 15) // 16 * 16
+    return int(ws[:count_bytes].view(torch.int32).abs().sum()) == 0
+
+
+# (n, k, rows, mode, residual), every stack at least 400 KB (rows x k, twice in
+# two-word mode): 4096 x 28672 at 8 two-word rows and 16 one-word rows (its own
+# one-word layout); 8 one-word rows in the two-word layout; the smallest k that
+# splits; 1000 rows (K in 8 parts); a ragged last range (4090 = 63 x 64 + 58);
+# 2048 rows; two rows on a long K; 130, 33 and 1 rows.
+_CASES = [(4096, 28672, 8, "i8x2", True), (4096, 28672, 16, "i8", False), (4096, 57344, 8, "i8", True),
+          (4096, 25600, 8, "i8x2", False), (1000, 28672, 8, "i8x2", True), (4090, 28672, 8, "i8x2", True),
+          (4090, 28672, 15, "i8", False), (2048, 32768, 7, "i8x2", True), (512, 131072, 2, "i8x2", True),
+          (130, 57344, 8, "i8x2", True), (33, 65536, 4, "i8x2", True), (1, 32768, 8, "i8x2", False)]
+
+
+@pytest.mark.parametrize("n,k,rows,mode,with_res", _CASES)
+def test_split_parity(n, k, rows, mode, with_res):
+    need = q8.matmul_rows_workspace_bytes(mode, n, k, rows)
+    say("k split", n, k, rows, mode, with_res, "workspace", need)
+    assert need > 0, "this shape splits K"
+    blocks, x, res = _case(n, k, rows, mode, with_res, seed=1500 + n % 101 + rows)
+    w = _dev(blocks)
+    hi, lo, sc = q8.quantize_act(mode, _dev(x))
+    resd = None if res is None else _dev(res)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    y = q8.matmul_rows_ws(mode, w, n, k, hi=hi, lo=lo, scale=sc, residual=resd, workspace=ws)
+    torch.cuda.synchronize()
+    assert _counters_zero(ws, n)
+    r, a = _expected(mode, blocks, n, k, x, res)
+    gate(y.cpu().numpy(), r, a, f"k split {n}x{k} rows={rows} {mode}")
+    # the same bits on every call, whatever order the workgroups arrive in
+    for _ in range(3):
+        y2 = q8.matmul_rows_ws(mode, w, n, k, hi=hi, lo=lo, scale=sc, residual=resd, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y2, y)
+    assert _counters_zero(ws, n)
+    # the unsplit projection passes the same gate; the two differ at most in
+    # the last bits of some outputs (f64 partials added in another order)
+    yu = q8.matmul_rows(mode, w, n, k, hi=hi, lo=lo, scale=sc, residual=resd)
+    torch.cuda.synchronize()
+    gate(yu.cpu().numpy(), r, a, f"unsplit {n}x{k} rows={rows} {mode}")
+
+
+def test_split_inplace_residual():
+    n, k, rows, mode = 4096, 28672, 8, "i8x2"
+    say("k split in place", n, k, rows, mode)
+    blocks, x, res = _case(n, k, rows, mode, True, seed=1700)
+    w = _dev(blocks)
+    hi, lo, sc = q8.quantize_act(mode, _dev(x))
+    ws = torch.zeros(q8.matmul_rows_workspace_bytes(mode, n, k, rows), dtype=torch.uint8, device="cuda")
+    ref = q8.matmul_rows_ws(mode, w, n, k, hi=hi, lo=lo, scale=sc, residual=_dev(res), workspace=ws)
+    h = _dev(res)
+    q8.matmul_rows_ws(mode, w, n, k, hi=hi, lo=lo, scale=sc, residual=h, out=h, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(h, ref)
+    r, a = _expected(mode, blocks, n, k, x, res)
+    gate(h.cpu().numpy(), r, a, "k split in place")
+
+
+def test_one_workspace_for_calls_of_different_shapes():
+    """Calls in a row on one workspace, with fewer, then more, then fewer row
+    ranges (the partials of one call cover bytes that are counters of no
+    other); every call equals its own run on a fresh zero-filled workspace."""
+    shapes = [(300, 28672, 8, "i8x2"), (4096, 28672, 8, "i8x2"), (2000, 32768, 7, "i8x2"),
+              (33, 28672, 16, "i8")]
+    big = max(q8.matmul_rows_workspace_bytes(m, n, k, r) for n, k, r, m in shapes)
+    shared = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    for i, (n, k, rows, mode) in enumerate(shapes):
+        say("shared workspace", n, k, rows, mode)
+        blocks, x, _ = _case(n, k, rows, mode, False, seed=1800 + i)
+        w = _dev(blocks)
+        hi, lo, sc = q8.quantize_act(mode, _dev(x))
+        y = q8.matmul_rows_ws(mode, w, n, k, hi=hi, lo=lo, scale=sc, workspace=shared)
+        fresh = torch.zeros(q8.matmul_rows_workspace_bytes(mode, n, k, rows), dtype=torch.uint8, device="cuda")
+        yf = q8.matmul_rows_ws(mode, w, n, k, hi=hi, lo=lo, scale=sc, workspace=fresh)
+        torch.cuda.synchronize()
+        assert torch.equal(y, yf)
+        assert _counters_zero(shared, n)
+        r, a = _expected(mode, blocks, n, k, x, None)
+        gate(y.cpu().numpy(), r, a, f"shared workspace {n}x{k} rows={rows} {mode}")
+
+
+@pytest.mark.parametrize("n,k,rows,mode", [(14336, 28672, 8, "i8x2"), (4096, 28672, 1, "i8x2"),
+                                           (4096, 28672, 9, "i8x2"), (4096, 28672, 24, "i8"),
+                                           (4096, 28672 - 64, 8, "i8x2"), (4096, 14336, 8, "i8x2"),
+                                           (4096, 28672, 8, "i8")])
+def test_calls_that_do_not_split_are_matmul_rows(n, k, rows, mode):
+    """No workspace needed: the call is q8_matmul_rows's, bit for bit, and a
+    workspace passed anyway is neither read nor written."""
+    say("no split", n, k, rows, mode)
+    assert q8.matmul_rows_workspace_bytes(mode, n, k, rows) == 0
+    blocks, x, _ = _case(n, k, rows, mode, False, seed=1900 + rows)
+    w = _dev(blocks)
+    hi, lo, sc = q8.quantize_act(mode, _dev(x))
+    ws = torch.full((4096,), 7, dtype=torch.uint8, device="cuda")
+    y = q8.matmul_rows_ws(mode, w, n, k, hi=hi, lo=lo, scale=sc, workspace=ws)
+    yu = q8.matmul_rows(mode, w, n, k, hi=hi, lo=lo, scale=sc)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yu)
+    assert bool((ws == 7).all())
+
+
+def test_split_inside_quantization_is_matmul_rows():
+    """A stack given as x is quantized inside the GEMV: no split, the workspace
+    untouched, the result that of q8_matmul_rows."""
+    n, k, rows, mode = 4096, 28672, 8, "i8x2"
+    say("k split with x", n, k, rows, mode)
+    blocks, x, _ = _case(n, k, rows, mode, False, seed=1950)
+    w, xd = _dev(blocks), _dev(x)
+    ws = torch.zeros(q8.matmul_rows_workspace_bytes(mode, n, k, rows), dtype=torch.uint8, device="cuda")
+    ws[:16] = 5
+    y = q8.matmul_rows_ws(mode, w, n, k, x=xd, workspace=ws)
+    yu = q8.matmul_rows(mode, w, n, k, x=xd)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yu)
+    assert int(ws[:16].sum()) == 16 * 5 and int(ws[16:].sum()) == 0
+
+
+def _capture(fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def test_split_graph_replays():
+    """Quantization and two split projections (residual on the second) captured
+    once and replayed four times with eager work between replays: every replay
+    equals the eager run bit for bit and passes the gate; counters stay zero."""
+    shapes = [(4096, 28672, 8, "i8x2", True), (1000, 28672, 16, "i8", False)]
+    bufs, want = [], []
+    for i, (n, k, rows, mode, with_res) in enumerate(shapes):
+        blocks, x, res = _case(n, k, rows, mode, with_res, seed=2000 + i)
+        want.append(_expected(mode, blocks, n, k, x, res))
+        hi = torch.empty((rows, k), dtype=torch.int8, device="cuda")
+        lo = torch.empty((rows, k), dtype=torch.int8, device="cuda") if mode == "i8x2" else None
+        sc = torch.empty((rows, k // 32), dtype=torch.float32, device="cuda")
+        ws = torch.zeros(q8.matmul_rows_workspace_bytes(mode, n, k, rows), dtype=torch.uint8, device="cuda")
+        y = torch.empty((rows, n), dtype=torch.float32, device="cuda")
+        bufs.append((n, k, rows, mode, _dev(blocks), _dev(x), None if res is None else _dev(res), hi, lo, sc, ws, y))
+
+    def step():
+        for n, k, rows, mode, w, x, res, hi, lo, sc, ws, y in bufs:
+            q8.quantize_act(mode, x, hi=hi, lo=lo, scale=sc)
+            q8.matmul_rows_ws(mode, w, n, k, hi=hi, lo=lo, scale=sc, residual=res, out=y, workspace=ws)
+
+    say("k split graph: capture")
+    step()
+    torch.cuda.synchronize()
+    ref = [b[-1].clone() for b in bufs]
+    g = _capture(step)
+    other = torch.zeros(1 << 20, device="cuda")
+    for replay in range(4):
+        for b in bufs:
+            b[-1].fill_(float("nan"))
+        other.add_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say("k split graph: replay", replay)
+        for (n, k, rows, mode, _), r, b, (rr, aa) in zip(shapes, ref, bufs, want):
+            assert torch.equal(b[-1], r), (replay, n, k, rows, mode)
+            assert _counters_zero(b[10], n)
+            gate(b[-1].cpu().numpy(), rr, aa, f"split replay {replay} {n}x{k} rows={rows} {mode}")
+    assert float(other[0]) == 4.0
