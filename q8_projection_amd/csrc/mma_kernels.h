@@ -398,8 +398,13 @@ __device__ __forceinline__ void compute_blocks(const uint8_t *slot, const BlockO
         math_block<RT, TT, WORDS, GR, GA, GB, SUMS>(op[j], offs[j].sel, acc, ma, sl, blk0 + offs[j].j);
 }
 
-template <int RT, int TT, int WORDS, int GR, int GA, int GB, bool SUMS>
-__global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_kernel(MmaArgs a) {
+// The shared-ring projection of one workgroup.  SPLIT: K split over a.ksplit
+// workgroups per row range, partials combined in a.ks_part (stacks of one
+// activation tile; launched as mma_split_kernel, so that mma_kernel carries
+// none of it).
+template <int RT, int TT, int WORDS, int GR, int GA, int GB, bool SUMS, bool SPLIT>
+__device__ __forceinline__ void mma_body(const MmaArgs &a) {
+    static_assert(!SPLIT || (!SUMS && TT == 1), "the K split serves projections of one activation tile");
     using L = Layout<RT, TT, WORDS, GR, GA, GB>;
     constexpr int W = L::W;
     constexpr int AT = L::kAT;
@@ -408,9 +413,7 @@ __global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_kernel(MmaArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     constexpr int RTW = L::kRTW;
     const int ga = wave % GA, gr = (wave / GA) % GR, gb = wave / (GA * GR);
-    // K split serves stacks of one activation tile only; other layouts compile without it
-    constexpr bool kCanSplit = !SUMS && TT == 1;
-    const int ksplit = kCanSplit ? a.ksplit : 1;
+    const int ksplit = SPLIT ? a.ksplit : 1;
     const uint32_t range = blockIdx.x / static_cast<uint32_t>(ksplit);
     const int split = static_cast<int>(blockIdx.x - range * static_cast<uint32_t>(ksplit));
     const int kc0 = split * a.nchunks;  // this workgroup's first chunk
@@ -523,7 +526,7 @@ __global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_kernel(MmaArgs a) {
     // reads the others' partials at agent scope, adds all of them in split
     // order (the same bits whichever workgroup is last), writes the outputs as
     // the unsplit kernel does, and returns the counter to zero.
-    if (kCanSplit && ksplit > 1) {
+    if (SPLIT) {
         __shared__ int ks_last;
         constexpr int kTot = RT * TT * L::kVals * 64;
         const size_t range_part = static_cast<size_t>(range) * ksplit * kTot;
@@ -603,6 +606,16 @@ __global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_kernel(MmaArgs a) {
             a.y[o] = static_cast<float>(tot * post + res);
         }
     }
+}
+
+template <int RT, int TT, int WORDS, int GR, int GA, int GB, bool SUMS>
+__global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_kernel(MmaArgs a) {
+    mma_body<RT, TT, WORDS, GR, GA, GB, SUMS, false>(a);
+}
+
+template <int RT, int TT, int WORDS, int GR, int GA, int GB>
+__global__ __launch_bounds__(64 * GR * GA * GB, 1) void mma_split_kernel(MmaArgs a) {
+    mma_body<RT, TT, WORDS, GR, GA, GB, false, true>(a);
 }
 
 // ------------------------------------------------ one tile, wave-private rings
@@ -725,8 +738,19 @@ template <int RT, int TT, int WORDS, int GR, int GA, int GB, bool SUMS>
 hipError_t run(const MmaArgs &a, hipStream_t stream) {
     using L = Layout<RT, TT, WORDS, GR, GA, GB>;
     if (L::kLdsBytes > device_info().lds_per_block) return hipErrorInvalidConfiguration;
-    const uint32_t grid = (a.n + a.rows_per_wg - 1) / a.rows_per_wg * static_cast<uint32_t>(a.ksplit);
+    const uint32_t grid = (a.n + a.rows_per_wg - 1) / a.rows_per_wg;
     hipLaunchKernelGGL((mma_kernel<RT, TT, WORDS, GR, GA, GB, SUMS>), dim3(grid), dim3(64 * L::W), L::kLdsBytes,
+                       stream, a);
+    return hipGetLastError();
+}
+
+// grid: a.ksplit workgroups for each range of a.rows_per_wg rows
+template <int RT, int TT, int WORDS, int GR, int GA, int GB>
+hipError_t run_ksplit(const MmaArgs &a, hipStream_t stream) {
+    using L = Layout<RT, TT, WORDS, GR, GA, GB>;
+    if (L::kLdsBytes > device_info().lds_per_block) return hipErrorInvalidConfiguration;
+    const uint32_t grid = (a.n + a.rows_per_wg - 1) / a.rows_per_wg * static_cast<uint32_t>(a.ksplit);
+    hipLaunchKernelGGL((mma_split_kernel<RT, TT, WORDS, GR, GA, GB>), dim3(grid), dim3(64 * L::W), L::kLdsBytes,
                        stream, a);
     return hipGetLastError();
 }
@@ -950,8 +974,9 @@ hipError_t launch_mma_ksplit_impl(int mode, const uint8_t *w, int64_t n, int64_t
     a.ksplit = p.ksplit;
     a.ks_count = static_cast<uint32_t *>(workspace);
     a.ks_part = reinterpret_cast<double *>(static_cast<uint8_t *>(workspace) + p.count_bytes);
-    if (p.words == 2) return run_split<2, 1, 4, false>(a, stream);
-    return run_split<1, 1, 4, false>(a, stream);
+    constexpr Split sp = wave_split(4, 1);
+    if (p.words == 2) return run_ksplit<4, 1, 2, sp.gr, sp.ga, sp.gb>(a, stream);
+    return run_ksplit<4, 1, 1, sp.gr, sp.ga, sp.gb>(a, stream);
 }
 
 }  // namespace
