@@ -147,11 +147,13 @@ class Prepared:
                            residual=self.res, out=self.y)
 
 
-def sweep(spec: str, dev, only_rows: int | None = None, launches: int = 0):
+def sweep(spec: str, dev, only_rows: int | None = None, launches: int = 0, ws: bool = False):
     """Kernel time of one projection per stack height (rows 1..64) through the
     library's own dispatch: "N,K,MODE", e.g. "14336,4096,i8x2".  Prints one JSON
     line per height.  With `only_rows`: run that height alone, eagerly,
-    `launches` times (for profilers), and print one line."""
+    `launches` times (for profilers), and print one line.  With `ws`: call
+    matmul_rows_ws with one zero-filled workspace for every height (the K split
+    where the library splits, matmul_rows elsewhere; `split` says which)."""
     import dataclasses
     import torch
     import q8_projection_amd as q8
@@ -160,9 +162,16 @@ def sweep(spec: str, dev, only_rows: int | None = None, launches: int = 0):
     base = wl.Call(f"sweep_{n}x{k}_{mode}", int(n), int(k), 64, mode, "matmul_rows", w_seed=900, x_seed=901)
     p = Prepared(base, dev)
     p.quantize()
+    need = {r: q8.matmul_rows_workspace_bytes(mode, base.n, base.k, r) if ws else 0 for r in range(1, 65)}
+    work = torch.zeros(max(16, *need.values()), dtype=torch.uint8, device=dev) if ws else None
 
     def launch(i, rows):
-        if mode == "f32":
+        if ws:
+            lo = None if p.lo is None else p.lo[:rows]
+            act = ({"x": p.x[:rows]} if mode == "f32" else
+                   {"hi": p.hi[:rows], "lo": lo, "scale": p.sc[:rows]})
+            q8.matmul_rows_ws(mode, p.w[i % p.copies], base.n, base.k, out=p.y[:rows], workspace=work, **act)
+        elif mode == "f32":
             q8.matmul_rows(mode, p.w[i % p.copies], base.n, base.k, x=p.x[:rows], out=p.y[:rows])
         else:
             lo = None if p.lo is None else p.lo[:rows]
@@ -177,18 +186,24 @@ def sweep(spec: str, dev, only_rows: int | None = None, launches: int = 0):
             launch(i, only_rows)
         torch.cuda.synchronize()
         call = dataclasses.replace(base, rows=only_rows)
-        print(json.dumps({"sweep": f"{n}x{k}", "mode": mode, "rows": only_rows, "launches": launches,
-                          "weight_bytes_per_launch": call.weight_bytes}), flush=True)
+        line = {"sweep": f"{n}x{k}", "mode": mode, "rows": only_rows, "launches": launches,
+                "weight_bytes_per_launch": call.weight_bytes}
+        if ws:
+            line.update(entry="matmul_rows_ws", split=need[only_rows] > 0)
+        print(json.dumps(line), flush=True)
         return
     for rows in (1, 2, 3, 4, 6, 8, 9, 12, 16, 24, 32, 48, 64):
         call = dataclasses.replace(base, rows=rows)
         reps = 20
         g = capture(lambda rows=rows: [launch(i, rows) for i in range(reps)])
         t = time_graph(g, 5) / reps
-        print(json.dumps({"sweep": f"{n}x{k}", "mode": mode, "rows": rows, "project_us": round(t * 1e6, 3),
-                          "GBps": round(call.weight_bytes / t / 1e9, 1),
-                          "pct_hbm_peak": round(call.weight_bytes / t / 1e9 / HBM_PEAK_GBPS * 100, 1),
-                          "rows_GFLOPs": round(call.flops / t / 1e9, 1)}), flush=True)
+        line = {"sweep": f"{n}x{k}", "mode": mode, "rows": rows, "project_us": round(t * 1e6, 3),
+                "GBps": round(call.weight_bytes / t / 1e9, 1),
+                "pct_hbm_peak": round(call.weight_bytes / t / 1e9 / HBM_PEAK_GBPS * 100, 1),
+                "rows_GFLOPs": round(call.flops / t / 1e9, 1)}
+        if ws:
+            line.update(entry="matmul_rows_ws", split=need[rows] > 0)
+        print(json.dumps(line), flush=True)
 
 
 def calib_copies(mib: int, dev) -> int:
@@ -521,6 +536,8 @@ def main(argv=None):
                     help="time one projection shape at stack heights 1..64 instead of the step")
     ap.add_argument("--rows", type=int, default=None,
                     help="with --sweep: run only this stack height, eagerly, warmup + steps launches (for profilers)")
+    ap.add_argument("--ws", action="store_true",
+                    help="with --sweep: call matmul_rows_ws (K split over workgroups where the library splits)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="with --only or --sweep --rows: also run torch's device copy of this many MiB, 4 times (the "
                          "known-size reference for HBM byte counters)")
@@ -538,7 +555,7 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.sweep:
-        sweep(args.sweep, dev, args.rows, args.warmup + args.steps)
+        sweep(args.sweep, dev, args.rows, args.warmup + args.steps, ws=args.ws)
         if args.rows is not None and args.calib_copy_mib:
             print(json.dumps({"calib_copy_bytes_each": calib_copies(args.calib_copy_mib, dev)}))
         return 0

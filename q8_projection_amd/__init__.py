@@ -203,8 +203,8 @@ def matmul_rows_workspace_bytes(mode, n: int, k: int, rows: int) -> int:
 
 def matmul_rows_ws(mode, w: torch.Tensor, n: int, k: int, hi=None, lo=None, scale=None, x=None,
                    residual=None, out=None, workspace=None, rows: int | None = None, stream=None) -> torch.Tensor:
-    """matmul_rows with K split across workgroups for short integer stacks on
-    short matrices (q8_matmul_rows_ws).  The workspace (uint8, at least
+    """matmul_rows with K split across workgroups for integer stacks on short
+    matrices (q8_matmul_rows_ws).  The workspace (uint8, at least
     matmul_rows_workspace_bytes) must start zero-filled; each call leaves its
     counters at zero, so a caller may keep one per stream and pass it every
     time.  None allocates a zero-filled one for this call."""

@@ -99,6 +99,27 @@ bool mma_serves(int mode, int64_t n, int64_t k, int rows, const void *w, const i
     return !quantize_inside && q8::mma_supports(mode, n, k, rows, w, hi, lo, scale);
 }
 
+// One slice of at most 64 rows of q8_matmul_rows (pointers at the slice's first
+// row): the int8 MFMA kernels, the f64 MFMA kernel, or the GEMV family 8 rows at
+// a time.
+hipError_t project_slice(int mode, const uint8_t *wb, int64_t n, int64_t k, int r, const int8_t *shi,
+                         const int8_t *slo, const float *ssc, const float *sx, const float *sres, float *sy,
+                         bool inside, hipStream_t st) {
+    if (mma_serves(mode, n, k, r, wb, shi, slo, ssc, inside))
+        return q8::launch_mma(mode, wb, n, k, r, shi, slo, ssc, sres, sy, n, st);
+    if (mode == Q8_ACT_F32 && q8::f64_mma_supports(n, k, r, sx))
+        return q8::launch_f64_mma(wb, n, k, r, sx, sres, sy, n, st);
+    const int64_t nb = k / 32;
+    hipError_t e = hipSuccess;
+    for (int c0 = 0; c0 < r && e == hipSuccess; c0 += 8) {
+        const int c = std::min(8, r - c0);
+        e = q8::launch_gemv(mode, wb, n, k, c, shi ? shi + c0 * k : nullptr, slo ? slo + c0 * k : nullptr,
+                            ssc ? ssc + c0 * nb : nullptr, sx ? sx + c0 * k : nullptr,
+                            sres ? sres + c0 * n : nullptr, sy + c0 * n, st);
+    }
+    return e;
+}
+
 }  // namespace
 
 namespace q8 {
@@ -185,22 +206,7 @@ q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t 
         const float *sx = (mode == Q8_ACT_F32 || inside) ? x + r0 * k : nullptr;
         const float *sres = residual ? residual + r0 * n : nullptr;
         float *sy = y + r0 * n;
-        hipError_t e;
-        if (mma_serves(mode, n, k, r, wb, shi, slo, ssc, inside)) {
-            e = q8::launch_mma(mode, wb, n, k, r, shi, slo, ssc, sres, sy, n, st);
-        } else if (mode == Q8_ACT_F32 && q8::f64_mma_supports(n, k, r, sx)) {
-            e = q8::launch_f64_mma(wb, n, k, r, sx, sres, sy, n, st);
-        } else {
-            // the GEMV family, 8 rows at a time
-            e = hipSuccess;
-            for (int c0 = 0; c0 < r && e == hipSuccess; c0 += 8) {
-                const int c = std::min(8, r - c0);
-                e = q8::launch_gemv(mode, wb, n, k, c, shi ? shi + c0 * k : nullptr, slo ? slo + c0 * k : nullptr,
-                                    ssc ? ssc + c0 * nb : nullptr, sx ? sx + c0 * k : nullptr,
-                                    sres ? sres + c0 * n : nullptr, sy + c0 * n, st);
-            }
-        }
-        if (e != hipSuccess) return Q8_E_HIP;
+        if (project_slice(mode, wb, n, k, r, shi, slo, ssc, sx, sres, sy, inside, st) != hipSuccess) return Q8_E_HIP;
     }
     return Q8_OK;
 }
@@ -212,8 +218,11 @@ q8_status q8_matvec(int mode, const void *w, int64_t n, int64_t k, const int8_t 
 
 int64_t q8_matmul_rows_workspace_bytes(int mode, int64_t n, int64_t k, int64_t rows) {
     if (mode != Q8_ACT_I8 && mode != Q8_ACT_I8X2) return 0;
-    if (check_sizes(n, k, rows) != Q8_OK || n < 1 || rows < 2 || rows > 64) return 0;
-    return q8::mma_ksplit_bytes(mode, n, k, static_cast<int>(rows));
+    if (check_sizes(n, k, rows) != Q8_OK || n < 1 || rows < 2) return 0;
+    // 64-row slices, one after another on the stream: the widest slice's size
+    const int64_t full = q8::mma_ksplit_bytes(mode, n, k, static_cast<int>(std::min<int64_t>(rows, 64)));
+    const int64_t tail = rows > 64 && rows % 64 ? q8::mma_ksplit_bytes(mode, n, k, static_cast<int>(rows % 64)) : 0;
+    return std::max(full, tail);
 }
 
 q8_status q8_matmul_rows_ws(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
@@ -237,12 +246,25 @@ q8_status q8_matmul_rows_ws(int mode, const void *w, int64_t n, int64_t k, int64
                                 residual ? rows * n * 4 : 0, rows * n * 4};
     for (int i = 0; i < 6; ++i)
         if (ins[i] && in_bytes[i] > 0 && overlap(workspace, need, ins[i], in_bytes[i])) return Q8_E_ALIAS;
-    const int r = static_cast<int>(rows);
-    if (!mma_serves(mode, n, k, r, w, hi, lo, scale, false))
-        return q8_matmul_rows(mode, w, n, k, rows, hi, lo, scale, x, residual, y, stream);
-    return from_hip(q8::launch_mma_ksplit(mode, static_cast<const uint8_t *>(w), n, k, r, hi,
-                                          mode == Q8_ACT_I8X2 ? lo : nullptr, scale, residual, y, workspace,
-                                          as_stream(stream)));
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const hipStream_t st = as_stream(stream);
+    // 64-row slices as in q8_matmul_rows; a slice that splits K uses the
+    // workspace (whose counters the previous slice has returned to zero)
+    for (int64_t r0 = 0; r0 < rows; r0 += 64) {
+        const int r = static_cast<int>(std::min<int64_t>(64, rows - r0));
+        const int8_t *shi = hi + r0 * k;
+        const int8_t *slo = mode == Q8_ACT_I8X2 ? lo + r0 * k : nullptr;
+        const float *ssc = scale + r0 * nb;
+        const float *sres = residual ? residual + r0 * n : nullptr;
+        float *sy = y + r0 * n;
+        hipError_t e;
+        if (q8::mma_ksplit_bytes(mode, n, k, r) > 0 && mma_serves(mode, n, k, r, wb, shi, slo, ssc, false))
+            e = q8::launch_mma_ksplit(mode, wb, n, k, r, shi, slo, ssc, sres, sy, workspace, st);
+        else
+            e = project_slice(mode, wb, n, k, r, shi, slo, ssc, nullptr, sres, sy, false, st);
+        if (e != hipSuccess) return Q8_E_HIP;
+    }
+    return Q8_OK;
 }
 
 int64_t q8_argmax_workspace_bytes(int64_t n) {

@@ -57,14 +57,13 @@ hipError_t launch_mma_sums(int mode, const uint8_t *w, int64_t n, int64_t k, int
 // run as row slices of under 1 GiB, one launch each.
 bool mma_supports(int mode, int64_t n, int64_t k, int rows, const void *w, const void *hi, const void *lo,
                   const void *scale);
-// The same projection with K split over workgroups, for stacks of one
-// activation tile (2..8 two-word rows, or one-word rows up to 16) on a matrix
-// short enough that launch_mma gives each workgroup a single 16-row tile: 64-row
-// ranges, each range's K split over 2, 4 or 8 workgroups whose f64 partials
-// meet in `workspace` and are added in split order by the last to arrive.
-// mma_ksplit_bytes: the workspace this call needs, 0 where it does not split
-// (then launch_mma serves it).  The workspace's counters must be zero before
-// the launch; the launch leaves them zero.
+// The same projection with K split over workgroups, for stacks of 2..64 rows
+// on a matrix short enough that launch_mma gives each workgroup a single
+// 16-row tile: 64-row ranges, each range's K split over 2, 4 or 8 workgroups
+// whose f64 partials meet in `workspace` and are added in split order by the
+// last to arrive.  mma_ksplit_bytes: the workspace this call needs, 0 where it
+// does not split (then launch_mma serves it).  The workspace's counters must be
+// zero before the launch; the launch leaves them zero.
 int64_t mma_ksplit_bytes(int mode, int64_t n, int64_t k, int rows);
 hipError_t launch_mma_ksplit(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
                              const int8_t *lo, const float *scale, const float *residual, float *y, void *workspace,

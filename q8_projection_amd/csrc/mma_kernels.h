@@ -66,6 +66,7 @@ constexpr int kWaveMaxRt = 1;     // single-tile stacks on matrices this short u
 constexpr int kWaveWaves = 8;
 constexpr int kWaveDepth = 2;
 constexpr int64_t kMaxMmaWeightBytes = int64_t(1) << 30;  // one launch's weights (buffer offsets < 2^31)
+constexpr int kMaxSplit = 8;  // workgroups one row range's K may be split over
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t *lds_ptr_t;
@@ -399,12 +400,11 @@ __device__ __forceinline__ void compute_blocks(const uint8_t *slot, const BlockO
 }
 
 // The shared-ring projection of one workgroup.  SPLIT: K split over a.ksplit
-// workgroups per row range, partials combined in a.ks_part (stacks of one
-// activation tile; launched as mma_split_kernel, so that mma_kernel carries
-// none of it).
+// workgroups per row range, partials combined in a.ks_part (launched as
+// mma_split_kernel, so that mma_kernel carries none of it).
 template <int RT, int TT, int WORDS, int GR, int GA, int GB, bool SUMS, bool SPLIT>
 __device__ __forceinline__ void mma_body(const MmaArgs &a) {
-    static_assert(!SPLIT || (!SUMS && TT == 1), "the K split serves projections of one activation tile");
+    static_assert(!SPLIT || !SUMS, "the block-sum export runs unsplit");
     using L = Layout<RT, TT, WORDS, GR, GA, GB>;
     constexpr int W = L::W;
     constexpr int AT = L::kAT;
@@ -523,9 +523,9 @@ __device__ __forceinline__ void mma_body(const MmaArgs &a) {
     // goes to the workspace as agent-scope atomic stores (written through this
     // XCD's L2 to the device-coherent level; no L2-wide write-back), completed
     // before the workgroup counts itself in.  The workgroup that counts last
-    // reads the others' partials at agent scope, adds all of them in split
-    // order (the same bits whichever workgroup is last), writes the outputs as
-    // the unsplit kernel does, and returns the counter to zero.
+    // reads every partial back at agent scope, adds them in split order (the
+    // same bits whichever workgroup is last), writes the outputs as the
+    // unsplit kernel does, and returns the counter to zero.
     if (SPLIT) {
         __shared__ int ks_last;
         constexpr int kTot = RT * TT * L::kVals * 64;
@@ -551,33 +551,34 @@ __device__ __forceinline__ void mma_body(const MmaArgs &a) {
         }
         __syncthreads();
         if (!ks_last) return;
-        if (gb == 0) {
+        // Every part is in the workspace, this workgroup's own included.  Each
+        // thread takes totals i = tid, tid + 64 W, ...: it issues the loads of
+        // all parts of them at once (parts past ksplit re-read the last one, so
+        // that every address stays inside the range), adds them in part order
+        // and parks the total in LDS where the unsplit kernel parks it.
+        constexpr int kPer = (kTot + 64 * W - 1) / (64 * W);
+        const double *parts = a.ks_part + range_part;
 #pragma unroll
-            for (int rt = 0; rt < RTW; ++rt)
+        for (int j = 0; j < kPer; ++j) {
+            const int i = static_cast<int>(threadIdx.x) + j * 64 * W;
+            if (i < kTot) {
+                double p[kMaxSplit];
 #pragma unroll
-                for (int t = 0; t < AT; ++t)
+                for (int s2 = 0; s2 < kMaxSplit; ++s2)
+                    p[s2] = __hip_atomic_load(parts + static_cast<size_t>(min(s2, ksplit - 1)) * kTot + i,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                double tot = p[0];
 #pragma unroll
-                    for (int v = 0; v < L::kVals; ++v) {
-                        const int idx = (((gr * RTW + rt) * TT + ga * AT + t) * L::kVals + v) * 64 + lane;
-                        double tot = 0.0;
-                        for (int s2 = 0; s2 < ksplit; ++s2) {
-                            const double p = s2 == split
-                                                 ? acc[rt][t][v]
-                                                 : __hip_atomic_load(a.ks_part + range_part +
-                                                                         static_cast<size_t>(s2) * kTot + idx,
-                                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            tot = s2 == 0 ? p : tot + p;
-                        }
-                        acc[rt][t][v] = tot;
-                    }
+                for (int s2 = 1; s2 < kMaxSplit; ++s2)
+                    if (s2 < ksplit) tot += p[s2];
+                red[i] = tot;
+            }
         }
         if (threadIdx.x == 0)
             __hip_atomic_store(a.ks_count + range, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-
-    // The waves of block group 0 hold the totals of their tiles; park them as
-    // [rt][tile][v][lane] and let every wave write a share of the outputs.
-    if (gb == 0) {
+    } else if (gb == 0) {
+        // The waves of block group 0 hold the totals of their tiles; park them
+        // as [rt][tile][v][lane] and let every wave write a share of the outputs.
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
@@ -887,30 +888,49 @@ hipError_t launch_mma_impl(int mode, const uint8_t *w, int64_t n, int64_t k, int
 
 // ------------------------------------------- K split over workgroups (workspace)
 //
-// A stack of one activation tile on a matrix of at most 16 rows per CU gets
-// one 16-row tile a workgroup from the dispatch above (the wave-private
-// kernel), so every workgroup copies the whole stack: as many bytes as its
-// weights.  With a caller workspace the same stack runs instead on the shared
+// On a matrix of at most 16 rows per CU the dispatch above gives each
+// workgroup one 16-row tile, so every workgroup copies the whole stack: as many
+// bytes as its weights at 8 two-word rows of a long K, and two to eight times
+// that for taller stacks; and a matrix of fewer than 16 rows per CU leaves CUs
+// idle.  With a caller workspace the same stack runs instead on the shared
 // ring with 64-row ranges and K split over ksplit workgroups per range
-// (ranges x ksplit about the CU count): each workgroup copies 1/ksplit of the
-// stack.  The combine costs the last workgroup of a range three memory round
-// trips in a row (its partial written through, the counter, the others'
-// partials read), about 2 us, so the split pays only where the stack a
-// workgroup would copy unsplit is large.  Measured (8 two-word rows, 4096 x k):
-// even at k = 16384-20480 (262-328 KB of stack), 0.7 us slower at 14336, 2 us
-// faster at 28672 (459 KB) and 6 us at 57344; two rows at 28672 (115 KB) 0.9
-// us slower; 1024-2048 rows, which leave CUs idle unsplit, 5 us faster at
-// 28672.  Hence the 400 KB floor below.
+// (ranges x ksplit at most the CU count): each workgroup copies 1/ksplit of the
+// stack.  The last workgroup of a range to finish reads every partial back and
+// adds them: its partial written through, the counter, then the loads of all
+// partials, one memory round trip each (a few for the widest stacks).
+//
+// When it pays (graphs of 20 launches, unsplit against split, two-word unless
+// noted):
+//  - Not when each workgroup gets fewer than 7 chunks: 4096 x 4096 loses at
+//    every height (8 rows 7.3 against 9.0 us, 64 rows 19.5 against 24.8), as
+//    do 2048 x 4096 and 1024 x 4096 beyond 9-32 rows.
+//  - Stacks of two or more activation tiles (9+ two-word, 17+ one-word rows),
+//    where the unsplit kernel is the shared ring with 16-row workgroups: 4096 x
+//    14336 16 rows 25.7 against 21.2 us, 32 rows 39.3 against 28.4, 64 rows
+//    58.2 against 47.5; one-word 32 rows 29.8 against 24.7; 4096 x 8192 16
+//    rows 15.6 against 14.5.
+//  - Matrices of at most 8 rows per CU (half the CUs idle unsplit), at any
+//    height, where the split spans at least half the CUs: 2048 x 14336 8 rows
+//    13.9 against 11.3, 1024 x 14336 13.2 against 10.4; not 512 x 14336 (64
+//    workgroups), 2-6 rows 9.2-9.4 against 9.6-9.7.
+//  - One tile on a full chip only for a large stack: 4096 x 14336 8 rows
+//    (224 KB) 16.1 both ways, 2-6 rows about 1 us slower split, one-word 9-12
+//    rows 1 us slower; 4096 x 28672 8 rows (448 KB) 29.5 against 27.4.
+// Inside these rules one case measured slower split: 4096 x 8192 at 48-64
+// one-word rows (23.4-23.8 against 24.9-25.3 us).
 //
 // The ranges' partials meet in the workspace: one u32 counter for each range
 // the largest such matrix can have (16 CUs' rows / 64, rounded up to 16
-// bytes), then f64 partials [ranges][ksplit][4 * kVals * 64].  The counters sit
-// where no call's partials go, so one workspace serves calls of any shape.
+// bytes), then f64 partials [ranges][ksplit][4 * TT * kVals * 64].  The
+// counters sit where no call's partials go, so one workspace serves calls of
+// any shape.
 
-constexpr int64_t kSplitMinStackBytes = 400 * 1024;  // rows x words x k of a stack that splits
+constexpr int kSplitMinChunks = 7;                    // chunks per workgroup of a split
+constexpr int64_t kSplitMinStackBytes = 400 * 1024;  // rows x words x k of a one-tile stack on a full chip
 
 struct KsPlan {
-    int words = 0;
+    int words = 0;           // words of the layout (one-word stacks of up to 8 rows run two-word)
+    int tt = 0;              // activation tiles
     int ksplit = 1;          // 1: no split for this stack
     int64_t ranges = 0;
     int64_t count_bytes = 0;
@@ -919,14 +939,13 @@ struct KsPlan {
 
 KsPlan ks_plan(int mode, int64_t n, int64_t k, int rows) {
     KsPlan p;
-    if ((mode != 1 && mode != 2) || n < 1 || rows < 1) return p;
+    if ((mode != 1 && mode != 2) || n < 1 || rows < 1 || rows > 64) return p;
     const bool as_two_word = mode == 1 && rows <= 8;
     const int words = mode == 2 || as_two_word ? 2 : 1;
     const int64_t nb = k / kBlock;
     const int64_t cus = std::max(1, device_info().cus);
-    if (act_tiles(words, rows) != 1 || n > 16 * cus || nb % kChunkBlocks != 0) return p;
+    if (n > 16 * cus || nb % kChunkBlocks != 0) return p;
     if (n * nb * kBlockBytes >= kMaxMmaWeightBytes) return p;
-    if (int64_t(rows) * (mode == 2 ? 2 : 1) * k < kSplitMinStackBytes) return p;
     const int64_t ranges = (n + 63) / 64;
     int split = 1;
     for (int c : {8, 4, 2})
@@ -934,14 +953,26 @@ KsPlan ks_plan(int mode, int64_t n, int64_t k, int rows) {
             split = c;
             break;
         }
-    if (split == 1) return p;
-    const int64_t tot = 4 * (words == 2 ? 2 : 4) * 64;  // RT * TT * kVals * 64 of Layout<4, 1, words, 4, 1, 4>
+    if (split == 1 || nb / (kChunkBlocks * split) < kSplitMinChunks) return p;
+    const int tt = act_tiles(words, rows);
+    // at most 8 rows per CU, split over at least half the CUs
+    const bool idle_cus = n <= 8 * cus && 2 * ranges * split >= cus;
+    const bool big_stack = int64_t(rows) * (mode == 2 ? 2 : 1) * k >= kSplitMinStackBytes;
+    if (tt == 1 && !idle_cus && !big_stack) return p;
+    const int64_t tot = 4 * tt * (words == 2 ? 2 : 4) * 64;  // RT * TT * kVals * 64 with RT = 4
     p.words = words;
+    p.tt = tt;
     p.ksplit = split;
     p.ranges = ranges;
     p.count_bytes = ((16 * cus + 63) / 64 * 4 + 15) / 16 * 16;
     p.bytes = p.count_bytes + ranges * split * tot * 8;
     return p;
+}
+
+template <int WORDS, int TT>
+hipError_t run_ksplit_tt(const MmaArgs &a, hipStream_t stream) {
+    constexpr Split sp = wave_split(4, TT);
+    return run_ksplit<4, TT, WORDS, sp.gr, sp.ga, sp.gb>(a, stream);
 }
 
 hipError_t launch_mma_ksplit_impl(int mode, const uint8_t *w, int64_t n, int64_t k, int rows, const int8_t *hi,
@@ -974,9 +1005,19 @@ hipError_t launch_mma_ksplit_impl(int mode, const uint8_t *w, int64_t n, int64_t
     a.ksplit = p.ksplit;
     a.ks_count = static_cast<uint32_t *>(workspace);
     a.ks_part = reinterpret_cast<double *>(static_cast<uint8_t *>(workspace) + p.count_bytes);
-    constexpr Split sp = wave_split(4, 1);
-    if (p.words == 2) return run_ksplit<4, 1, 2, sp.gr, sp.ga, sp.gb>(a, stream);
-    return run_ksplit<4, 1, 1, sp.gr, sp.ga, sp.gb>(a, stream);
+    if (p.words == 2) {
+        switch (p.tt) {
+            case 1: return run_ksplit_tt<2, 1>(a, stream);
+            case 2: return run_ksplit_tt<2, 2>(a, stream);
+            case 4: return run_ksplit_tt<2, 4>(a, stream);
+            default: return run_ksplit_tt<2, 8>(a, stream);
+        }
+    }
+    switch (p.tt) {
+        case 1: return run_ksplit_tt<1, 1>(a, stream);
+        case 2: return run_ksplit_tt<1, 2>(a, stream);
+        default: return run_ksplit_tt<1, 4>(a, stream);
+    }
 }
 
 }  // namespace

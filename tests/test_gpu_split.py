@@ -52,15 +52,25 @@ def _counters_zero(ws, n):
     return int(ws[:count_bytes].view(torch.int32).abs().sum()) == 0
 
 
-# (n, k, rows, mode, residual), every stack at least 400 KB (rows x k, twice in
-# two-word mode): 4096 x 28672 at 8 two-word rows and 16 one-word rows (its own
-# one-word layout); 8 one-word rows in the two-word layout; the smallest k that
-# splits; 1000 rows (K in 8 parts); a ragged last range (4090 = 63 x 64 + 58);
-# 2048 rows; two rows on a long K; 130, 33 and 1 rows.
+# (n, k, rows, mode, residual).  One activation tile, stacks of at least 400 KB
+# (rows x k, twice in two-word mode) or at most 8 rows per CU: 4096 x 28672 at
+# 8 two-word rows and 16 one-word rows; 8 one-word rows in the two-word layout;
+# the smallest k that splits; 1000 rows (K in 8 parts); a ragged last range
+# (4090 = 63 x 64 + 58); 2048 rows; two rows on a long K; 130, 33 and 1 rows;
+# 2048 x 14336 at 2 two-word and 5 one-word rows.  Several tiles: the down
+# projection 4096 x 14336 at 16 two-word rows (two tiles), 33 and 64 one-word
+# rows (four), 64 two-word rows (eight); 50 two-word rows of 2000 x 14336
+# (eight tiles, the last half empty); 25 one-word rows on a ragged n.  More
+# than 64 rows: 100 two-word rows (two split slices), 70 one-word rows (a
+# split slice, then 6 rows that do not split).
 _CASES = [(4096, 28672, 8, "i8x2", True), (4096, 28672, 16, "i8", False), (4096, 57344, 8, "i8", True),
           (4096, 25600, 8, "i8x2", False), (1000, 28672, 8, "i8x2", True), (4090, 28672, 8, "i8x2", True),
           (4090, 28672, 15, "i8", False), (2048, 32768, 7, "i8x2", True), (512, 131072, 2, "i8x2", True),
-          (130, 57344, 8, "i8x2", True), (33, 65536, 4, "i8x2", True), (1, 32768, 8, "i8x2", False)]
+          (130, 57344, 8, "i8x2", True), (33, 65536, 4, "i8x2", True), (1, 32768, 8, "i8x2", False),
+          (2048, 14336, 2, "i8x2", True), (2048, 14336, 5, "i8", False),
+          (4096, 14336, 16, "i8x2", True), (4096, 14336, 33, "i8", True), (4096, 14336, 64, "i8", False),
+          (4096, 14336, 64, "i8x2", True), (2000, 14336, 50, "i8x2", False), (4090, 16384, 25, "i8", True),
+          (4096, 14336, 100, "i8x2", True), (4096, 14336, 70, "i8", False)]
 
 
 @pytest.mark.parametrize("n,k,rows,mode,with_res", _CASES)
@@ -111,8 +121,8 @@ def test_one_workspace_for_calls_of_different_shapes():
     """Calls in a row on one workspace, with fewer, then more, then fewer row
     ranges (the partials of one call cover bytes that are counters of no
     other); every call equals its own run on a fresh zero-filled workspace."""
-    shapes = [(300, 28672, 8, "i8x2"), (4096, 28672, 8, "i8x2"), (2000, 32768, 7, "i8x2"),
-              (33, 28672, 16, "i8")]
+    shapes = [(300, 28672, 8, "i8x2"), (4096, 14336, 64, "i8x2"), (2000, 32768, 7, "i8x2"),
+              (4096, 14336, 33, "i8"), (33, 28672, 16, "i8")]
     big = max(q8.matmul_rows_workspace_bytes(m, n, k, r) for n, k, r, m in shapes)
     shared = torch.zeros(big, dtype=torch.uint8, device="cuda")
     for i, (n, k, rows, mode) in enumerate(shapes):
@@ -131,7 +141,7 @@ def test_one_workspace_for_calls_of_different_shapes():
 
 
 @pytest.mark.parametrize("n,k,rows,mode", [(14336, 28672, 8, "i8x2"), (4096, 28672, 1, "i8x2"),
-                                           (4096, 28672, 9, "i8x2"), (4096, 28672, 24, "i8"),
+                                           (4096, 14336, 16, "i8"), (4096, 4096, 48, "i8x2"),
                                            (4096, 28672 - 64, 8, "i8x2"), (4096, 14336, 8, "i8x2"),
                                            (4096, 28672, 8, "i8")])
 def test_calls_that_do_not_split_are_matmul_rows(n, k, rows, mode):
@@ -184,7 +194,7 @@ def test_split_graph_replays():
     """Quantization and two split projections (residual on the second) captured
     once and replayed four times with eager work between replays: every replay
     equals the eager run bit for bit and passes the gate; counters stay zero."""
-    shapes = [(4096, 28672, 8, "i8x2", True), (1000, 28672, 16, "i8", False)]
+    shapes = [(4096, 28672, 8, "i8x2", True), (1000, 28672, 16, "i8", False), (4096, 14336, 64, "i8x2", True)]
     bufs, want = [], []
     for i, (n, k, rows, mode, with_res) in enumerate(shapes):
         blocks, x, res = _case(n, k, rows, mode, with_res, seed=2000 + i)
