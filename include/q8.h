@@ -152,33 +152,38 @@ q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t 
                          const int8_t *lo, const float *scale, const float *x, const float *residual,
                          float *y, void *stream);
 
-/* q8_matmul_rows with a caller workspace that lets integer stacks split K
- * across workgroups on short matrices: the batched decode step's and the
- * prefill's projections (model::author page, Functions: decode_batch,
- * prefill) on a matrix of at most 16 rows per CU, such as a layer's down
- * projection (4096 x 14336).  There q8_matmul_rows gives every workgroup one
- * 16-row tile and the whole stack, so each workgroup copies the stack (as many
- * bytes as its weights at 8 two-word rows of 14336, up to eight times that at
- * 64 rows), and a matrix of fewer rows leaves CUs idle.  This call gives each
- * 64-row range's K to 2, 4 or 8 workgroups, which copy 1/2 .. 1/8 of the stack
- * each.  Their f64 partial sums meet in the workspace and the last workgroup
- * of a range to finish (told by an atomic counter) adds them in split order,
- * so the result does not depend on the order of arrival; its f64 sums are
- * added in another order than q8_matmul_rows's, so the two may differ in the
- * last bits of an output.  The combine costs the last workgroup of each range
- * a few memory round trips, so a slice splits only where that measured to pay:
- * each part at least 7 chunks of 256 columns, and either a stack of two or
- * more activation tiles (over 8 two-word or 16 one-word rows), a matrix of at
- * most 8 rows per CU whose split spans at least half the CUs, or a stack of at
- * least 400 KB (rows x k bytes, twice in Q8_ACT_I8X2).  Measured on 4096 x 14336 two-word: 16 rows 21.2 against 25.7
- * us, 32 rows 28.4 against 39.3, 64 rows 47.5 against 58.2; on 2048 x 14336,
- * 8 rows 11.3 against 13.9.  Stacks of more than 64 rows run as 64-row slices,
- * one after another, each split or not on its own.
+/* q8_matmul_rows with a caller workspace that lets stacks split K across
+ * workgroups on short matrices: the batched decode step's and the prefill's
+ * projections (model::author page, Functions: decode_batch, prefill) on a
+ * matrix of at most 16 rows per CU, such as a layer's down projection (4096 x
+ * 14336).  There q8_matmul_rows gives every workgroup one 16-row tile and the
+ * whole stack, so each workgroup copies the stack (as many bytes as its
+ * weights at 8 two-word rows of 14336, up to eight times that at 64 rows), and
+ * a matrix of fewer rows leaves CUs idle.  This call gives each row range's K
+ * to 2, 4 or 8 workgroups, which copy 1/2 .. 1/8 of the stack each (integer
+ * modes: 64-row ranges on int8 matrix cores; f32 mode, 5..64 rows: 32-row
+ * ranges on f64 matrix cores).  Their f64 partial sums meet in the workspace
+ * and the last workgroup of a range to finish (told by an atomic counter) adds
+ * them in split order, so the result does not depend on the order of arrival;
+ * its f64 sums are added in another order than q8_matmul_rows's, so the two
+ * may differ in the last bits of an output.  The combine costs the last
+ * workgroup of each range a few memory round trips, so a slice splits only
+ * where that measured to pay.  Integer modes: each part at least 7 chunks of
+ * 256 columns, and either a stack of two or more activation tiles (over 8
+ * two-word or 16 one-word rows), a matrix of at most 8 rows per CU whose split
+ * spans at least half the CUs, or a stack of at least 400 KB (rows x k bytes,
+ * twice in Q8_ACT_I8X2).  f32 mode: each part at least 16 blocks, and 128 for
+ * stacks of up to 16 rows on matrices of more than 8 rows per CU.  Measured on
+ * 4096 x 14336: two-word 16 rows 20.7 against 24.6 us, 32 rows 27.7 against
+ * 36.3, 64 rows 43.4 against 54.3; f32 16 rows 47.3 against 55.2, 64 rows
+ * 126.2 against 139.8; on 2048 x 14336, two-word 8 rows 11.3 against 13.9, f32
+ * 64 rows 70.1 against 138.9.  Stacks of more than 64 rows run as 64-row
+ * slices, one after another, each split or not on its own.
  * Arguments as q8_matmul_rows, plus:
  *   workspace       : device memory, 16-byte aligned, of at least
  *                     q8_matmul_rows_workspace_bytes(mode, n, k, rows) bytes,
  *                     zero-filled by the caller before its first use.  It
- *                     starts with 32-bit counters, one for each 64-row range
+ *                     starts with 32-bit counters, one for each 16-row tile
  *                     the tallest matrix that splits can have on this device
  *                     (16 rows per CU), which every call leaves at zero again;
  *                     the rest is scratch.  So one workspace, as large as the
@@ -186,12 +191,13 @@ q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t 
  *                     without clearing, but two calls in flight at once must
  *                     not share it.
  *   workspace_bytes : its size in bytes.
- * Where q8_matmul_rows_workspace_bytes is 0 (f32 mode, one row, more than 16
- * rows per CU, no 64-row slice that splits by the rule above, k not a multiple
- * of 256, weights of 1 GiB or more), for a stack given as x, and for slices
- * q8_matmul_rows would not run on its MFMA kernels (16-byte alignment), the
- * call or slice is q8_matmul_rows's and the workspace is not read or written
- * (it may be NULL where no slice splits).
+ * Where q8_matmul_rows_workspace_bytes is 0 (one row, f32 stacks under 5
+ * rows, more than 16 rows per CU, no 64-row slice that splits by the rules
+ * above, integer k not a multiple of 256, weights of 1 GiB or more), for an
+ * integer stack given as x, and for slices q8_matmul_rows would not run on its
+ * matrix-core kernels (16-byte alignment), the call or slice is
+ * q8_matmul_rows's and the workspace is not read or written (it may be NULL
+ * where no slice splits).
  * Errors: as q8_matmul_rows; with a workspace needed: Q8_E_NULL (none given),
  * Q8_E_ALIGN, Q8_E_SHAPE (workspace_bytes too small), Q8_E_ALIAS (workspace
  * overlapping an input or y). */

@@ -217,11 +217,14 @@ q8_status q8_matvec(int mode, const void *w, int64_t n, int64_t k, const int8_t 
 }
 
 int64_t q8_matmul_rows_workspace_bytes(int mode, int64_t n, int64_t k, int64_t rows) {
-    if (mode != Q8_ACT_I8 && mode != Q8_ACT_I8X2) return 0;
+    if (mode != Q8_ACT_F32 && mode != Q8_ACT_I8 && mode != Q8_ACT_I8X2) return 0;
     if (check_sizes(n, k, rows) != Q8_OK || n < 1 || rows < 2) return 0;
     // 64-row slices, one after another on the stream: the widest slice's size
-    const int64_t full = q8::mma_ksplit_bytes(mode, n, k, static_cast<int>(std::min<int64_t>(rows, 64)));
-    const int64_t tail = rows > 64 && rows % 64 ? q8::mma_ksplit_bytes(mode, n, k, static_cast<int>(rows % 64)) : 0;
+    const auto bytes = [&](int r) {
+        return mode == Q8_ACT_F32 ? q8::f64_ksplit_bytes(n, k, r) : q8::mma_ksplit_bytes(mode, n, k, r);
+    };
+    const int64_t full = bytes(static_cast<int>(std::min<int64_t>(rows, 64)));
+    const int64_t tail = rows > 64 && rows % 64 ? bytes(static_cast<int>(rows % 64)) : 0;
     return std::max(full, tail);
 }
 
@@ -241,10 +244,12 @@ q8_status q8_matmul_rows_ws(int mode, const void *w, int64_t n, int64_t k, int64
     if (!aligned(workspace, 16)) return Q8_E_ALIGN;
     if (workspace_bytes < need) return Q8_E_SHAPE;
     const int64_t nb = k / 32;
-    const void *ins[] = {w, hi, lo, scale, residual, y};
+    const bool f32 = mode == Q8_ACT_F32;
+    const void *ins[] = {w, f32 ? nullptr : hi, f32 ? nullptr : lo, f32 ? nullptr : scale, f32 ? x : nullptr,
+                         residual, y};
     const int64_t in_bytes[] = {n * nb * 34, rows * k, mode == Q8_ACT_I8X2 ? rows * k : 0, rows * nb * 4,
-                                residual ? rows * n * 4 : 0, rows * n * 4};
-    for (int i = 0; i < 6; ++i)
+                                rows * k * 4, residual ? rows * n * 4 : 0, rows * n * 4};
+    for (int i = 0; i < 7; ++i)
         if (ins[i] && in_bytes[i] > 0 && overlap(workspace, need, ins[i], in_bytes[i])) return Q8_E_ALIAS;
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const hipStream_t st = as_stream(stream);
@@ -252,16 +257,19 @@ q8_status q8_matmul_rows_ws(int mode, const void *w, int64_t n, int64_t k, int64
     // workspace (whose counters the previous slice has returned to zero)
     for (int64_t r0 = 0; r0 < rows; r0 += 64) {
         const int r = static_cast<int>(std::min<int64_t>(64, rows - r0));
-        const int8_t *shi = hi + r0 * k;
+        const int8_t *shi = f32 ? nullptr : hi + r0 * k;
         const int8_t *slo = mode == Q8_ACT_I8X2 ? lo + r0 * k : nullptr;
-        const float *ssc = scale + r0 * nb;
+        const float *ssc = f32 ? nullptr : scale + r0 * nb;
+        const float *sx = f32 ? x + r0 * k : nullptr;
         const float *sres = residual ? residual + r0 * n : nullptr;
         float *sy = y + r0 * n;
         hipError_t e;
-        if (q8::mma_ksplit_bytes(mode, n, k, r) > 0 && mma_serves(mode, n, k, r, wb, shi, slo, ssc, false))
+        if (f32 && q8::f64_ksplit_bytes(n, k, r) > 0 && q8::f64_mma_supports(n, k, r, sx))
+            e = q8::launch_f64_mma_ksplit(wb, n, k, r, sx, sres, sy, workspace, st);
+        else if (!f32 && q8::mma_ksplit_bytes(mode, n, k, r) > 0 && mma_serves(mode, n, k, r, wb, shi, slo, ssc, false))
             e = q8::launch_mma_ksplit(mode, wb, n, k, r, shi, slo, ssc, sres, sy, workspace, st);
         else
-            e = project_slice(mode, wb, n, k, r, shi, slo, ssc, nullptr, sres, sy, false, st);
+            e = project_slice(mode, wb, n, k, r, shi, slo, ssc, sx, sres, sy, false, st);
         if (e != hipSuccess) return Q8_E_HIP;
     }
     return Q8_OK;

@@ -40,6 +40,7 @@ constexpr int64_t kMaxK = int64_t(1) << 22;           // keeps 65 rows of x unde
 // Below 5 rows the f64 GEMV is faster (4 rows of 4096 x 4096: 14 us against
 // about 16 us here); from 5 rows on it falls far behind (43 us at 6 rows).
 constexpr int kMinRows = 5;
+constexpr int kSplitMinBlocks = 16;  // blocks per workgroup of a split: two per wave
 
 typedef double v4d __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
@@ -56,6 +57,12 @@ struct F64Args {
     uint32_t nb;
     uint32_t w_bytes;        // n * nb * 34
     int rows;                // activation rows (5..64)
+    // K split over workgroups (f64_mma_split_kernel): workgroup g takes weight
+    // tile range g / ksplit and blocks [nb / ksplit * (g % ksplit), + nb / ksplit);
+    // the ranges' partial totals meet in a caller workspace.
+    int ksplit;
+    double *ks_part;         // [ranges][ksplit][RT * AT * 4 * 64] f64 partials
+    uint32_t *ks_count;      // [ranges] arrivals, zero between calls
 };
 
 // One block's operands for this lane: for each of its RT weight rows the
@@ -140,16 +147,22 @@ __device__ __forceinline__ void math_block(const Ops<RT, AT> &o, uint32_t b, int
 constexpr size_t park_bytes(int rt, int at) { return size_t(kWaves - 1) * rt * at * 4 * 64 * sizeof(double); }
 
 // RT 16-row weight tiles per workgroup (each wave covers all of them),
-// AT 16-row activation tiles.
-template <int RT, int AT>
-__global__ __launch_bounds__(kThreads) void f64_mma_kernel(F64Args a) {
+// AT 16-row activation tiles.  SPLIT: this workgroup takes 1/ksplit of K for
+// its tiles, and the last of a range's workgroups to finish adds the partial
+// totals (launched as f64_mma_split_kernel, so that f64_mma_kernel carries none
+// of it).
+template <int RT, int AT, bool SPLIT>
+__device__ __forceinline__ void f64_body(const F64Args &a) {
     constexpr int D = 8 / (RT * AT);  // blocks per chunk: 64 MFMAs of work between a chunk's loads and its use
     __shared__ double park[kWaves - 1][RT][AT][4][64];
     static_assert(sizeof(park) == park_bytes(RT, AT));
     const int lane = threadIdx.x & 63;
     const int lane_row4 = (lane & 15) << 2;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t row = blockIdx.x * (16u * RT) + static_cast<uint32_t>(lane & 15);
+    const int ksplit = SPLIT ? a.ksplit : 1;
+    const uint32_t range = blockIdx.x / static_cast<uint32_t>(ksplit);
+    const uint32_t split = blockIdx.x - range * static_cast<uint32_t>(ksplit);
+    const uint32_t row = range * (16u * RT) + static_cast<uint32_t>(lane & 15);
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.w), 0, a.w_bytes, kBufferDword3);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
@@ -168,10 +181,11 @@ __global__ __launch_bounds__(kThreads) void f64_mma_kernel(F64Args a) {
     // remain, so every refill it issues reads at least one live block; the
     // last one or two chunks are finished after it without refills.  Blocks
     // past the wave's last read zeros and add exact zeros.
-    const int nb = static_cast<int>(a.nb);
+    const int nb = static_cast<int>(a.nb) / ksplit;  // this workgroup's blocks: kb0 .. kb0 + nb - 1
+    const uint32_t kb0 = split * static_cast<uint32_t>(nb);
     const int mine = wave < nb ? (nb - wave + kWaves - 1) / kWaves : 0;
     const int last = std::max(mine - 1, 0);
-    auto block_of = [&](int j) { return static_cast<uint32_t>(wave + kWaves * std::min(j, last)); };
+    auto block_of = [&](int j) { return kb0 + static_cast<uint32_t>(wave + kWaves * std::min(j, last)); };
     Ops<RT, AT> ping[D], pong[D];
 #pragma unroll
     for (int c = 0; c < D; ++c) load_ops<RT, AT>(a, rw, rx, row, block_of(c), lane, c < mine, ping[c]);
@@ -217,7 +231,81 @@ __global__ __launch_bounds__(kThreads) void f64_mma_kernel(F64Args a) {
                 for (int v = 0; v < 4; ++v) park[wave - 1][rt][t][v][lane] = acc[rt][t][v];
     }
     __syncthreads();
-    if (wave != 0 || row >= a.n) return;
+    if constexpr (!SPLIT) {
+        if (wave != 0 || row >= a.n) return;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const uint32_t wrow = row + 16 * rt;
+            if (rt > 0 && wrow >= a.n) continue;
+#pragma unroll
+            for (int t = 0; t < AT; ++t)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    double tot = acc[rt][t][v];
+#pragma unroll
+                    for (int w = 0; w < kWaves - 1; ++w) tot += park[w][rt][t][v][lane];
+                    const int r = t * 16 + (lane >> 4) + 4 * v;
+                    if (r >= a.rows) continue;
+                    const int64_t o = static_cast<int64_t>(r) * a.ldy + wrow;
+                    const double res = a.residual ? static_cast<double>(a.residual[o]) : 0.0;
+                    a.y[o] = static_cast<float>(tot + res);
+                }
+        }
+        return;
+    }
+    if (wave != 0) return;
+    // wave 0's totals, in wave order (as the unsplit kernel adds them), in place
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int t = 0; t < AT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int w = 0; w < kWaves - 1; ++w) acc[rt][t][v] += park[w][rt][t][v][lane];
+    {
+        // K split: these totals are one of ksplit parts of the range's.  Wave 0 writes
+        // them to the workspace as agent-scope atomic stores (through the XCD's
+        // L2 to the device-coherent level) and waits for them; lane 0 then
+        // counts the workgroup in.  The last to count reads every part back
+        // (its own included), all of one part's loads in flight at once, and
+        // adds them in part order: the same bits whichever workgroup is last.
+        constexpr int kTot = RT * AT * 4 * 64;
+        double *parts = a.ks_part + static_cast<size_t>(range) * ksplit * kTot;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int t = 0; t < AT; ++t)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    __hip_atomic_store(parts + static_cast<size_t>(split) * kTot + ((rt * AT + t) * 4 + v) * 64 + lane,
+                                       acc[rt][t][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        uint32_t done = 0;
+        if (lane == 0) done = __hip_atomic_fetch_add(a.ks_count + range, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        done = __builtin_amdgcn_readfirstlane(done);
+        if (done != static_cast<uint32_t>(ksplit - 1)) return;
+        for (int s2 = 0; s2 < ksplit; ++s2) {
+            double p[RT][AT][4];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int t = 0; t < AT; ++t)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        p[rt][t][v] = __hip_atomic_load(
+                            parts + static_cast<size_t>(s2) * kTot + ((rt * AT + t) * 4 + v) * 64 + lane,
+                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int t = 0; t < AT; ++t)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[rt][t][v] = s2 == 0 ? p[rt][t][v] : acc[rt][t][v] + p[rt][t][v];
+        }
+        if (lane == 0) __hip_atomic_store(a.ks_count + range, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (row >= a.n) return;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const uint32_t wrow = row + 16 * rt;
@@ -226,16 +314,23 @@ __global__ __launch_bounds__(kThreads) void f64_mma_kernel(F64Args a) {
         for (int t = 0; t < AT; ++t)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                double tot = acc[rt][t][v];
-#pragma unroll
-                for (int w = 0; w < kWaves - 1; ++w) tot += park[w][rt][t][v][lane];
                 const int r = t * 16 + (lane >> 4) + 4 * v;
                 if (r >= a.rows) continue;
                 const int64_t o = static_cast<int64_t>(r) * a.ldy + wrow;
                 const double res = a.residual ? static_cast<double>(a.residual[o]) : 0.0;
-                a.y[o] = static_cast<float>(tot + res);
+                a.y[o] = static_cast<float>(acc[rt][t][v] + res);
             }
     }
+}
+
+template <int RT, int AT>
+__global__ __launch_bounds__(kThreads) void f64_mma_kernel(F64Args a) {
+    f64_body<RT, AT, false>(a);
+}
+
+template <int RT, int AT>
+__global__ __launch_bounds__(kThreads) void f64_mma_split_kernel(F64Args a) {
+    f64_body<RT, AT, true>(a);
 }
 
 template <int RT, int AT>
@@ -258,6 +353,55 @@ hipError_t run(const F64Args &a, hipStream_t stream) {
     return hipSuccess;
 }
 
+// K split: two 16-row weight tiles a workgroup (each activation load and
+// conversion feeding two MFMA chains, as on tall matrices) over a range's
+// ksplit parts of K, for matrices where the unsplit launch keeps one tile a
+// workgroup (at most 16 rows per CU).  Measured (graphs of 20 launches,
+// unsplit against split): 4096 x 14336 16 rows 55.0 against 47.4 us, 64 rows
+// 139.8 against 126.2; 2048 x 14336 64 rows 139.4 against 69.5 (the unsplit
+// launch fills half the CUs); 1024 x 14336 64 rows 138.1 against 43.6; 4096 x
+// 4096 64 rows 46.3 against 43.8.  Not taken for one activation tile on a
+// full chip with under 128 blocks a part: 4096 x 4096 at 6-12 rows measured
+// 16.5-17.4 against 17.1-17.5 us.
+struct F64Split {
+    int at = 0;
+    int ksplit = 1;          // 1: no split
+    int64_t ranges = 0;
+    int64_t bytes = 0;
+};
+
+F64Split f64_split_plan(int64_t n, int64_t k, int rows) {
+    F64Split p;
+    const DeviceInfo dev = device_info();
+    const int64_t cus = std::max(1, dev.cus);
+    if (rows < kMinRows || rows > 64 || n < 1 || k < 64 || k % 64 != 0 || k > kMaxK) return p;
+    if (n > 16 * cus || n * (k / kBlock) * kBlockBytes > kMaxWeightBytes) return p;
+    const int at = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
+    if (park_bytes(2, at) > static_cast<size_t>(dev.lds_per_block)) return p;
+    const int64_t nb = k / kBlock;
+    const int64_t ranges = (n + 31) / 32;
+    int split = 1;
+    for (int c : {8, 4, 2})
+        if (ranges * c <= cus && nb % c == 0 && nb / c >= kSplitMinBlocks) {
+            split = c;
+            break;
+        }
+    if (split == 1) return p;
+    if (at == 1 && n > 8 * cus && nb / split < 128) return p;
+    p.at = at;
+    p.ksplit = split;
+    p.ranges = ranges;
+    p.bytes = split_count_bytes(static_cast<int>(cus)) + ranges * split * (2 * at * 4 * 64) * 8;
+    return p;
+}
+
+template <int AT>
+hipError_t run_split(const F64Args &a, hipStream_t stream) {
+    const unsigned grid = static_cast<unsigned>((a.n + 31) / 32 * a.ksplit);
+    f64_mma_split_kernel<2, AT><<<grid, kThreads, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool f64_mma_supports(int64_t n, int64_t k, int rows, const void *x) {
@@ -278,6 +422,9 @@ hipError_t launch_f64_mma(const uint8_t *w, int64_t n, int64_t k, int rows, cons
     a.nb = static_cast<uint32_t>(k / kBlock);
     a.w_bytes = 0;
     a.rows = rows;
+    a.ksplit = 1;
+    a.ks_part = nullptr;
+    a.ks_count = nullptr;
     // Two weight tiles a workgroup where that takes fewer rounds of
     // workgroups over the CUs, at about 1.65 times the time of a one-tile
     // round: each activation load and conversion then feeds two MFMA chains.
@@ -289,6 +436,35 @@ hipError_t launch_f64_mma(const uint8_t *w, int64_t n, int64_t k, int rows, cons
     if (rows <= 32) return two ? run<2, 2>(a, stream) : run<1, 2>(a, stream);
     if (two && park_bytes(2, 4) <= static_cast<size_t>(dev.lds_per_block)) return run<2, 4>(a, stream);
     return run<1, 4>(a, stream);
+}
+
+int64_t f64_ksplit_bytes(int64_t n, int64_t k, int rows) {
+    const F64Split p = f64_split_plan(n, k, rows);
+    return p.ksplit > 1 ? p.bytes : 0;
+}
+
+hipError_t launch_f64_mma_ksplit(const uint8_t *w, int64_t n, int64_t k, int rows, const float *x,
+                                 const float *residual, float *y, void *workspace, hipStream_t stream) {
+    const F64Split p = f64_split_plan(n, k, rows);
+    if (p.ksplit <= 1 || !workspace) return hipErrorInvalidValue;
+    F64Args a;
+    a.w = w;
+    a.x = x;
+    a.residual = residual;
+    a.y = y;
+    a.ldy = n;
+    a.n = static_cast<uint32_t>(n);
+    a.k = static_cast<uint32_t>(k);
+    a.nb = static_cast<uint32_t>(k / kBlock);
+    a.w_bytes = static_cast<uint32_t>(n * (k / kBlock) * kBlockBytes);
+    a.rows = rows;
+    a.ksplit = p.ksplit;
+    a.ks_count = static_cast<uint32_t *>(workspace);
+    a.ks_part = reinterpret_cast<double *>(static_cast<uint8_t *>(workspace) +
+                                           split_count_bytes(std::max(1, device_info().cus)));
+    if (p.at == 1) return run_split<1>(a, stream);
+    if (p.at == 2) return run_split<2>(a, stream);
+    return run_split<4>(a, stream);
 }
 
 }  // namespace q8

@@ -14,6 +14,11 @@ struct DeviceInfo {
 };
 DeviceInfo device_info();
 
+// Bytes of the counters at the head of a K-split workspace: one u32 per 16-row
+// tile of the tallest matrix that splits (16 rows per CU), so that every
+// split's row ranges find their counters there, rounded up to 16 bytes.
+inline int64_t split_count_bytes(int cus) { return (int64_t(cus) * 4 + 15) / 16 * 16; }
+
 hipError_t launch_quantize_weights(const float *w, int64_t n, int64_t k, uint8_t *blocks,
                                    hipStream_t stream);
 hipError_t launch_quantize_act(int words, const float *x, int64_t rows, int64_t k, int8_t *hi,
@@ -74,6 +79,15 @@ hipError_t launch_mma_ksplit(int mode, const uint8_t *w, int64_t n, int64_t k, i
 // ldy.  Needs what f64_mma_supports needs.
 hipError_t launch_f64_mma(const uint8_t *w, int64_t n, int64_t k, int rows, const float *x, const float *residual,
                           float *y, int64_t ldy, hipStream_t stream);
+// The f32 stack with K split over workgroups, for matrices of at most 16 rows
+// per CU (where launch_f64_mma keeps one weight tile a workgroup): two tiles a
+// workgroup, each range's K over 2, 4 or 8 workgroups, partials combined in
+// split order in `workspace` as launch_mma_ksplit does.  f64_ksplit_bytes: the
+// workspace it needs, 0 where it does not split.  y and residual have row
+// stride n.
+int64_t f64_ksplit_bytes(int64_t n, int64_t k, int rows);
+hipError_t launch_f64_mma_ksplit(const uint8_t *w, int64_t n, int64_t k, int rows, const float *x,
+                                 const float *residual, float *y, void *workspace, hipStream_t stream);
 // Whether launch_f64_mma serves this stack: 5..64 rows, n >= 1, k a multiple of
 // 64 up to 2^22, x 16-byte aligned.
 bool f64_mma_supports(int64_t n, int64_t k, int rows, const void *x);

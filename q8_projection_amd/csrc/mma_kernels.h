@@ -919,11 +919,11 @@ hipError_t launch_mma_impl(int mode, const uint8_t *w, int64_t n, int64_t k, int
 // Inside these rules one case measured slower split: 4096 x 8192 at 48-64
 // one-word rows (23.4-23.8 against 24.9-25.3 us).
 //
-// The ranges' partials meet in the workspace: one u32 counter for each range
-// the largest such matrix can have (16 CUs' rows / 64, rounded up to 16
-// bytes), then f64 partials [ranges][ksplit][4 * TT * kVals * 64].  The
-// counters sit where no call's partials go, so one workspace serves calls of
-// any shape.
+// The ranges' partials meet in the workspace: the counters (split_count_bytes:
+// one u32 per 16-row tile of the tallest matrix that splits, which covers the
+// ranges of every split kernel), then f64 partials [ranges][ksplit][4 * TT *
+// kVals * 64].  The counters sit where no call's partials go, so one workspace
+// serves calls of any shape.
 
 constexpr int kSplitMinChunks = 7;                    // chunks per workgroup of a split
 constexpr int64_t kSplitMinStackBytes = 400 * 1024;  // rows x words x k of a one-tile stack on a full chip
@@ -964,7 +964,7 @@ KsPlan ks_plan(int mode, int64_t n, int64_t k, int rows) {
     p.tt = tt;
     p.ksplit = split;
     p.ranges = ranges;
-    p.count_bytes = ((16 * cus + 63) / 64 * 4 + 15) / 16 * 16;
+    p.count_bytes = split_count_bytes(static_cast<int>(cus));
     p.bytes = p.count_bytes + ranges * split * tot * 8;
     return p;
 }

@@ -156,30 +156,31 @@ def _ma(mode=1, w=BASE, n=64, k=256, hi=BASE + 16 * MB, lo=BASE + 32 * MB, scale
 
 
 def test_split_workspace_size():
-    """Workspace of the K-split projection: 32-bit counters for the 64-row
-    ranges of the tallest matrix that splits (16 rows per CU: 64 counters, 256
-    bytes, on a 256-CU device), then the f64 partials of every split of every
-    range: 4 tiles of 16 weight rows by the activation tiles' rows (8 per
-    two-word tile, 16 per one-word tile).  The device count of CUs is 256 here
-    (MI355X, and the value assumed with no device)."""
+    """Workspace of the K-split projection: 32-bit counters, one per 16-row tile
+    of the tallest matrix that splits (16 rows per CU: 256 counters, 1024 bytes,
+    on a 256-CU device), then the f64 partials of every split of every range:
+    integer modes 4 tiles of 16 weight rows by the activation tiles' rows (8 per
+    two-word tile, 16 per one-word tile); f32 mode 2 tiles of 16 weight rows by
+    16 rows per activation tile.  The device count of CUs is 256 here (MI355X,
+    and the value assumed with no device)."""
     f = q8.lib().q8_matmul_rows_workspace_bytes
     part = lambda tiles, rows_per_tile: 4 * 16 * tiles * rows_per_tile * 8
     # 4096 x 28672, 8 two-word rows: 64 ranges, K in 4 parts (64 x 8 > 256 CUs)
-    assert f(2, 4096, 28672, 8) == 256 + 64 * 4 * part(1, 8)
+    assert f(2, 4096, 28672, 8) == 1024 + 64 * 4 * part(1, 8)
     # 9 two-word rows: two tiles
-    assert f(2, 4096, 28672, 9) == 256 + 64 * 4 * part(2, 8)
+    assert f(2, 4096, 28672, 9) == 1024 + 64 * 4 * part(2, 8)
     # 16 one-word rows: one tile of 16; 17: two
-    assert f(1, 4096, 28672, 16) == 256 + 64 * 4 * part(1, 16)
-    assert f(1, 4096, 28672, 17) == 256 + 64 * 4 * part(2, 16)
+    assert f(1, 4096, 28672, 16) == 1024 + 64 * 4 * part(1, 16)
+    assert f(1, 4096, 28672, 17) == 1024 + 64 * 4 * part(2, 16)
     # one-word rows up to 8 run in the two-word layout; 8 x 57344 bytes of stack
     assert f(1, 4096, 57344, 8) == f(2, 4096, 28672, 8)
     # 1000 rows: 16 ranges, K in 8 parts (nb = 896 is a multiple of 64)
-    assert f(2, 1000, 28672, 8) == 256 + 16 * 8 * part(1, 8)
+    assert f(2, 1000, 28672, 8) == 1024 + 16 * 8 * part(1, 8)
     # the down projection 4096 x 14336: 16 two-word rows (459 KB), 64 one-word
     # rows (917 KB, four tiles) and 64 two-word rows (eight tiles)
-    assert f(2, 4096, 14336, 16) == 256 + 64 * 4 * part(2, 8)
-    assert f(1, 4096, 14336, 64) == 256 + 64 * 4 * part(4, 16)
-    assert f(2, 4096, 14336, 64) == 256 + 64 * 4 * part(8, 8)
+    assert f(2, 4096, 14336, 16) == 1024 + 64 * 4 * part(2, 8)
+    assert f(1, 4096, 14336, 64) == 1024 + 64 * 4 * part(4, 16)
+    assert f(2, 4096, 14336, 64) == 1024 + 64 * 4 * part(8, 8)
     # more than 64 rows: 64-row slices one after another, the widest one's size
     assert f(2, 4096, 14336, 100) == f(2, 4096, 14336, 64)
     assert f(2, 4096, 14336, 65) == f(2, 4096, 14336, 64)
@@ -189,17 +190,30 @@ def test_split_workspace_size():
     assert f(1, 4096, 25600, 16) > 0 and f(1, 4096, 25600, 15) == 0
     # at most 8 rows per CU, split over at least half the CUs: any height from
     # 2 rows, given 7 chunks a workgroup (512 rows: 64 workgroups, too few)
-    assert f(2, 2048, 14336, 2) == 256 + 32 * 8 * part(1, 8)
-    assert f(1, 1024, 14336, 3) == 256 + 16 * 8 * part(1, 8)
-    assert f(2, 512, 14336, 8) == 0 and f(2, 512, 14336, 9) == 256 + 8 * 8 * part(2, 8)
+    assert f(2, 2048, 14336, 2) == 1024 + 32 * 8 * part(1, 8)
+    assert f(1, 1024, 14336, 3) == 1024 + 16 * 8 * part(1, 8)
+    assert f(2, 512, 14336, 8) == 0 and f(2, 512, 14336, 9) == 1024 + 8 * 8 * part(2, 8)
     # no split: f32 mode, one row, tall matrix, one tile on a full chip under
     # 400 KB (the down projection at 8 two-word rows: 229 KB; 16 one-word rows),
     # fewer than 7 chunks a workgroup (4096 x 4096, 2048 x 4096), K not in
     # whole chunks per part, k not a multiple of 256, bad sizes
-    for args in ((0, 4096, 28672, 8), (2, 4096, 28672, 1), (2, 14336, 28672, 8), (2, 4096, 14336, 8),
+    for args in ((2, 4096, 28672, 1), (2, 14336, 28672, 8), (2, 4096, 14336, 8),
                  (1, 4096, 14336, 16), (2, 4096, 4096, 48), (2, 2048, 4096, 8), (1, 4096, 28672, 8),
                  (2, 4096, 25344, 16), (2, 4096, 28672 - 64, 8), (2, 0, 28672, 8), (2, 4096, 28672, 0),
                  (2, -1, 28672, 8), (2, 4096, 100, 8), (7, 4096, 28672, 8)):
+        assert f(*args) == 0, args
+    # f32 mode: two weight tiles a workgroup over 32-row ranges, on matrices of
+    # at most 16 rows per CU, from 5 rows (the f64 matrix-core kernel's floor)
+    f32part = lambda tiles: 2 * 16 * tiles * 16 * 8
+    assert f(0, 4096, 8192, 16) == 1024 + 128 * 2 * f32part(1)
+    assert f(0, 4096, 4096, 24) == 1024 + 128 * 2 * f32part(2)
+    # (32 rows: two activation tiles; 64-row plans need 112 KiB of LDS, more
+    # than the 64 KiB assumed with no device)
+    assert f(0, 2048, 4096, 32) == 1024 + 64 * 4 * f32part(2)
+    # (no split: under 5 rows, tall matrix, one activation tile on a full chip
+    # with under 128 blocks a part, bad k)
+    for args in ((0, 4096, 4096, 4), (0, 4096, 4096, 1), (0, 14336, 4096, 16), (0, 4096, 4096, 16),
+                 (0, 4096, 100, 16)):
         assert f(*args) == 0, args
 
 

@@ -41,8 +41,19 @@ def _case(n, k, rows, mode, with_res, seed):
 
 
 def _expected(mode, blocks, n, k, x, res):
+    if mode == "f32":
+        return oracle.project(mode, blocks, n, k, x.shape[0], x=x, residual=res)
     hi, lo, sc = oracle.quantize_act(mode, x)
     return oracle.project(mode, blocks, n, k, x.shape[0], hi=hi, lo=lo, scale=sc, residual=res)
+
+
+def _stack(mode, xd):
+    """The stack's arguments to a projection: x itself in the f32 mode, else
+    its quantization on the GPU."""
+    if mode == "f32":
+        return {"x": xd}
+    hi, lo, sc = q8.quantize_act(mode, xd)
+    return {"hi": hi, "lo": lo, "scale": sc}
 
 
 def _counters_zero(ws, n):
@@ -62,7 +73,10 @@ def _counters_zero(ws, n):
 # rows (four), 64 two-word rows (eight); 50 two-word rows of 2000 x 14336
 # (eight tiles, the last half empty); 25 one-word rows on a ragged n.  More
 # than 64 rows: 100 two-word rows (two split slices), 70 one-word rows (a
-# split slice, then 6 rows that do not split).
+# split slice, then 6 rows that do not split).  The f32 mode (f64 matrix
+# cores, two weight tiles a workgroup): 16 rows of 4096 x 8192, 64 of 4096 x
+# 4096, 24 rows of 2048 x 14336, 5 rows on a ragged n, 33 rows, and 100 rows
+# in two slices.
 _CASES = [(4096, 28672, 8, "i8x2", True), (4096, 28672, 16, "i8", False), (4096, 57344, 8, "i8", True),
           (4096, 25600, 8, "i8x2", False), (1000, 28672, 8, "i8x2", True), (4090, 28672, 8, "i8x2", True),
           (4090, 28672, 15, "i8", False), (2048, 32768, 7, "i8x2", True), (512, 131072, 2, "i8x2", True),
@@ -70,7 +84,9 @@ _CASES = [(4096, 28672, 8, "i8x2", True), (4096, 28672, 16, "i8", False), (4096,
           (2048, 14336, 2, "i8x2", True), (2048, 14336, 5, "i8", False),
           (4096, 14336, 16, "i8x2", True), (4096, 14336, 33, "i8", True), (4096, 14336, 64, "i8", False),
           (4096, 14336, 64, "i8x2", True), (2000, 14336, 50, "i8x2", False), (4090, 16384, 25, "i8", True),
-          (4096, 14336, 100, "i8x2", True), (4096, 14336, 70, "i8", False)]
+          (4096, 14336, 100, "i8x2", True), (4096, 14336, 70, "i8", False),
+          (4096, 8192, 16, "f32", True), (4096, 4096, 64, "f32", False), (2048, 14336, 24, "f32", True),
+          (4090, 8192, 5, "f32", True), (1000, 8192, 33, "f32", False), (4096, 14336, 100, "f32", True)]
 
 
 @pytest.mark.parametrize("n,k,rows,mode,with_res", _CASES)
@@ -80,23 +96,23 @@ def test_split_parity(n, k, rows, mode, with_res):
     assert need > 0, "this shape splits K"
     blocks, x, res = _case(n, k, rows, mode, with_res, seed=1500 + n % 101 + rows)
     w = _dev(blocks)
-    hi, lo, sc = q8.quantize_act(mode, _dev(x))
+    act = _stack(mode, _dev(x))
     resd = None if res is None else _dev(res)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
-    y = q8.matmul_rows_ws(mode, w, n, k, hi=hi, lo=lo, scale=sc, residual=resd, workspace=ws)
+    y = q8.matmul_rows_ws(mode, w, n, k, residual=resd, workspace=ws, **act)
     torch.cuda.synchronize()
     assert _counters_zero(ws, n)
     r, a = _expected(mode, blocks, n, k, x, res)
     gate(y.cpu().numpy(), r, a, f"k split {n}x{k} rows={rows} {mode}")
     # the same bits on every call, whatever order the workgroups arrive in
     for _ in range(3):
-        y2 = q8.matmul_rows_ws(mode, w, n, k, hi=hi, lo=lo, scale=sc, residual=resd, workspace=ws)
+        y2 = q8.matmul_rows_ws(mode, w, n, k, residual=resd, workspace=ws, **act)
         torch.cuda.synchronize()
         assert torch.equal(y2, y)
     assert _counters_zero(ws, n)
     # the unsplit projection passes the same gate; the two differ at most in
     # the last bits of some outputs (f64 partials added in another order)
-    yu = q8.matmul_rows(mode, w, n, k, hi=hi, lo=lo, scale=sc, residual=resd)
+    yu = q8.matmul_rows(mode, w, n, k, residual=resd, **act)
     torch.cuda.synchronize()
     gate(yu.cpu().numpy(), r, a, f"unsplit {n}x{k} rows={rows} {mode}")
 
@@ -191,10 +207,11 @@ def _capture(fn):
 
 
 def test_split_graph_replays():
-    """Quantization and two split projections (residual on the second) captured
+    """Quantization and four split projections (one in the f32 mode) captured
     once and replayed four times with eager work between replays: every replay
     equals the eager run bit for bit and passes the gate; counters stay zero."""
-    shapes = [(4096, 28672, 8, "i8x2", True), (1000, 28672, 16, "i8", False), (4096, 14336, 64, "i8x2", True)]
+    shapes = [(4096, 28672, 8, "i8x2", True), (1000, 28672, 16, "i8", False), (4096, 14336, 64, "i8x2", True),
+              (4096, 4096, 24, "f32", True)]
     bufs, want = [], []
     for i, (n, k, rows, mode, with_res) in enumerate(shapes):
         blocks, x, res = _case(n, k, rows, mode, with_res, seed=2000 + i)
@@ -208,6 +225,9 @@ def test_split_graph_replays():
 
     def step():
         for n, k, rows, mode, w, x, res, hi, lo, sc, ws, y in bufs:
+            if mode == "f32":
+                q8.matmul_rows_ws(mode, w, n, k, x=x, residual=res, out=y, workspace=ws)
+                continue
             q8.quantize_act(mode, x, hi=hi, lo=lo, scale=sc)
             q8.matmul_rows_ws(mode, w, n, k, hi=hi, lo=lo, scale=sc, residual=res, out=y, workspace=ws)
 
