@@ -66,7 +66,6 @@ constexpr int kWaveMaxRt = 1;     // single-tile stacks on matrices this short u
 constexpr int kWaveWaves = 8;
 constexpr int kWaveDepth = 2;
 constexpr int64_t kMaxMmaWeightBytes = int64_t(1) << 30;  // one launch's weights (buffer offsets < 2^31)
-constexpr int kMaxSplit = 8;  // workgroups one row range's K may be split over
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t *lds_ptr_t;
@@ -399,6 +398,42 @@ __device__ __forceinline__ void compute_blocks(const uint8_t *slot, const BlockO
         math_block<RT, TT, WORDS, GR, GA, GB, SUMS>(op[j], offs[j].sel, acc, ma, sl, blk0 + offs[j].j);
 }
 
+// The last workgroup of a split range: total i = sum over parts s (in order) of
+// parts[s * kTot + i], into red[i].  Thread t takes i = t, t + T, ...; it
+// issues the agent-scope loads of a group of G of its totals (all KS parts of
+// each, at most 16 loads) at once, so the combine costs one memory round trip
+// per group instead of one per load.
+template <int KS, int kTot, int T>
+__device__ __forceinline__ void combine_parts(const double *parts, double *red) {
+    constexpr int kPer = (kTot + T - 1) / T;
+    constexpr int G = KS >= 16 ? 1 : 16 / KS;
+    const int t = static_cast<int>(threadIdx.x);
+#pragma unroll
+    for (int j0 = 0; j0 < kPer; j0 += G) {
+        double p[G][KS];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int i = t + (j0 + g) * T;
+            if (j0 + g < kPer && i < kTot) {
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    p[g][s] = __hip_atomic_load(parts + static_cast<size_t>(s) * kTot + i, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int i = t + (j0 + g) * T;
+            if (j0 + g < kPer && i < kTot) {
+                double tot = p[g][0];
+#pragma unroll
+                for (int s = 1; s < KS; ++s) tot += p[g][s];
+                red[i] = tot;
+            }
+        }
+    }
+}
+
 // The shared-ring projection of one workgroup.  SPLIT: K split over a.ksplit
 // workgroups per row range, partials combined in a.ks_part (launched as
 // mma_split_kernel, so that mma_kernel carries none of it).
@@ -551,29 +586,15 @@ __device__ __forceinline__ void mma_body(const MmaArgs &a) {
         }
         __syncthreads();
         if (!ks_last) return;
-        // Every part is in the workspace, this workgroup's own included.  Each
-        // thread takes totals i = tid, tid + 64 W, ...: it issues the loads of
-        // all parts of them at once (parts past ksplit re-read the last one, so
-        // that every address stays inside the range), adds them in part order
-        // and parks the total in LDS where the unsplit kernel parks it.
-        constexpr int kPer = (kTot + 64 * W - 1) / (64 * W);
+        // Every part is in the workspace, this workgroup's own included: add
+        // them in part order into LDS, where the unsplit kernel parks its totals.
         const double *parts = a.ks_part + range_part;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int i = static_cast<int>(threadIdx.x) + j * 64 * W;
-            if (i < kTot) {
-                double p[kMaxSplit];
-#pragma unroll
-                for (int s2 = 0; s2 < kMaxSplit; ++s2)
-                    p[s2] = __hip_atomic_load(parts + static_cast<size_t>(min(s2, ksplit - 1)) * kTot + i,
-                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                double tot = p[0];
-#pragma unroll
-                for (int s2 = 1; s2 < kMaxSplit; ++s2)
-                    if (s2 < ksplit) tot += p[s2];
-                red[i] = tot;
-            }
-        }
+        if (ksplit == 2)
+            combine_parts<2, kTot, 64 * W>(parts, red);
+        else if (ksplit == 4)
+            combine_parts<4, kTot, 64 * W>(parts, red);
+        else
+            combine_parts<8, kTot, 64 * W>(parts, red);
         if (threadIdx.x == 0)
             __hip_atomic_store(a.ks_count + range, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else if (gb == 0) {
@@ -944,8 +965,8 @@ KsPlan ks_plan(int mode, int64_t n, int64_t k, int rows) {
     const int words = mode == 2 || as_two_word ? 2 : 1;
     const int64_t nb = k / kBlock;
     const int64_t cus = std::max(1, device_info().cus);
-    if (n > 16 * cus || nb % kChunkBlocks != 0) return p;
-    if (n * nb * kBlockBytes >= kMaxMmaWeightBytes) return p;
+    if (nb % kChunkBlocks != 0 || n * nb * kBlockBytes >= kMaxMmaWeightBytes) return p;
+    if (n > 16 * cus) return p;
     const int64_t ranges = (n + 63) / 64;
     int split = 1;
     for (int c : {8, 4, 2})

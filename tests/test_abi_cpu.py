@@ -197,7 +197,7 @@ def test_split_workspace_size():
     # 400 KB (the down projection at 8 two-word rows: 229 KB; 16 one-word rows),
     # fewer than 7 chunks a workgroup (4096 x 4096, 2048 x 4096), K not in
     # whole chunks per part, k not a multiple of 256, bad sizes
-    for args in ((2, 4096, 28672, 1), (2, 14336, 28672, 8), (2, 4096, 14336, 8),
+    for args in ((2, 4096, 28672, 1), (2, 14336, 2048, 8), (2, 4096, 14336, 8),
                  (1, 4096, 14336, 16), (2, 4096, 4096, 48), (2, 2048, 4096, 8), (1, 4096, 28672, 8),
                  (2, 4096, 25344, 16), (2, 4096, 28672 - 64, 8), (2, 0, 28672, 8), (2, 4096, 28672, 0),
                  (2, -1, 28672, 8), (2, 4096, 100, 8), (7, 4096, 28672, 8)):
