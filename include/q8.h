@@ -174,11 +174,12 @@ q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t 
  * spans at least half the CUs, or a stack of at least 400 KB (rows x k bytes,
  * twice in Q8_ACT_I8X2).  f32 mode: each part at least 16 blocks, and 128 for
  * stacks of up to 16 rows on matrices of more than 8 rows per CU.  Measured on
- * 4096 x 14336: two-word 16 rows 20.7 against 24.6 us, 32 rows 27.7 against
- * 36.3, 64 rows 43.4 against 54.3; f32 16 rows 47.3 against 55.2, 64 rows
- * 126.2 against 139.8; on 2048 x 14336, two-word 8 rows 11.3 against 13.9, f32
- * 64 rows 70.1 against 138.9.  Stacks of more than 64 rows run as 64-row
- * slices, one after another, each split or not on its own.
+ * 4096 x 14336 (unsplit against split, varying by about 1 us between runs):
+ * two-word 16 rows 25 against 21 us, 32 rows 36-38 against 27-28, 64 rows
+ * 54 against 44; f32 16 rows 55 against 47, 64 rows 139 against 126; on 2048 x
+ * 14336, two-word 8 rows 14 against 11.5, f32 64 rows 138 against 69.  Stacks
+ * of more than 64 rows run as 64-row slices, one after another, each split or
+ * not on its own.
  * Arguments as q8_matmul_rows, plus:
  *   workspace       : device memory, 16-byte aligned, of at least
  *                     q8_matmul_rows_workspace_bytes(mode, n, k, rows) bytes,
