@@ -146,7 +146,8 @@ q8_status q8_matvec(int mode, const void *w, int64_t n, int64_t k, const int8_t 
  * stack given as x (hi, lo, scale NULL) is quantized inside the projection as
  * in q8_matvec, for at most 8 rows (one GEMV pass); a taller one is
  * Q8_E_SHAPE: quantize it once with q8_quantize_act (the result serves every
- * projection of the same input) and pass hi, lo and scale.
+ * projection of the same input) and pass hi, lo and scale.  On a matrix of at
+ * most 16 rows per CU, q8_matmul_rows_ws (below) is faster for most stacks.
  * Errors: Q8_E_NULL, Q8_E_SHAPE, Q8_E_ALIGN, Q8_E_MODE, Q8_E_ALIAS, Q8_E_HIP. */
 q8_status q8_matmul_rows(int mode, const void *w, int64_t n, int64_t k, int64_t rows, const int8_t *hi,
                          const int8_t *lo, const float *scale, const float *x, const float *residual,

@@ -250,3 +250,27 @@ def test_split_graph_replays():
             assert _counters_zero(b[10], n)
             gate(b[-1].cpu().numpy(), rr, aa, f"split replay {replay} {n}x{k} rows={rows} {mode}")
     assert float(other[0]) == 4.0
+
+
+def test_split_misaligned_weights_run_unsplit():
+    """Weights that q8_matmul_rows cannot give its matrix-core kernels (4-byte
+    but not 16-byte aligned) run on q8_matmul_rows's path, bit for bit, and
+    leave the workspace alone."""
+    n, k, rows, mode = 4096, 14336, 16, "i8x2"
+    say("k split, misaligned weights", n, k, rows, mode)
+    blocks, x, _ = _case(n, k, rows, mode, False, seed=2100)
+    nbytes = blocks.size
+    wbuf = torch.empty(nbytes + 16, dtype=torch.uint8, device="cuda")
+    wbuf[4:4 + nbytes].copy_(_dev(blocks).reshape(-1))
+    w4 = wbuf[4:4 + nbytes]
+    hi, lo, sc = q8.quantize_act(mode, _dev(x))
+    need = q8.matmul_rows_workspace_bytes(mode, n, k, rows)
+    assert need > 0
+    ws = torch.full((need,), 3, dtype=torch.uint8, device="cuda")
+    y = q8.matmul_rows_ws(mode, w4, n, k, hi=hi, lo=lo, scale=sc, workspace=ws)
+    yu = q8.matmul_rows(mode, w4, n, k, hi=hi, lo=lo, scale=sc)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yu)
+    assert bool((ws == 3).all())
+    r, a = _expected(mode, blocks, n, k, x, None)
+    gate(y.cpu().numpy(), r, a, "k split, misaligned weights")
