@@ -146,6 +146,38 @@ __device__ __forceinline__ void math_block(const Ops<RT, AT> &o, uint32_t b, int
 // LDS of the waves' partial sums: 112 KiB at two weight and four activation tiles.
 constexpr size_t park_bytes(int rt, int at) { return size_t(kWaves - 1) * rt * at * 4 * 64 * sizeof(double); }
 
+// The last workgroup of a split range, wave 0: total f (= (rt AT + t) 4 + v)
+// of this lane = sum over parts s (in order) of parts[s * kTot + 64 f + lane],
+// into acc[rt][t][v].  The loads of a group of totals, all KS parts of each (at
+// most 32 loads), are issued at once: one memory round trip per group.
+template <int KS, int RT, int AT>
+__device__ __forceinline__ void combine_parts(const double *parts, int lane, v4d (&acc)[RT][AT]) {
+    constexpr int NV = RT * AT * 4;
+    constexpr int kTot = NV * 64;
+    constexpr int G = 32 / KS < NV ? 32 / KS : NV;
+#pragma unroll
+    for (int f0 = 0; f0 < NV; f0 += G) {
+        double p[G][KS];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            if (f0 + g < NV) {
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    p[g][s] = __hip_atomic_load(parts + static_cast<size_t>(s) * kTot + (f0 + g) * 64 + lane,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            if (f0 + g < NV) {
+                double t = p[g][0];
+#pragma unroll
+                for (int s = 1; s < KS; ++s) t += p[g][s];
+                const int f = f0 + g;
+                acc[f / (AT * 4)][(f / 4) % AT][f % 4] = t;
+            }
+    }
+}
+
 // RT 16-row weight tiles per workgroup (each wave covers all of them),
 // AT 16-row activation tiles.  SPLIT: this workgroup takes 1/ksplit of K for
 // its tiles, and the last of a range's workgroups to finish adds the partial
@@ -268,8 +300,8 @@ __device__ __forceinline__ void f64_body(const F64Args &a) {
         // them to the workspace as agent-scope atomic stores (through the XCD's
         // L2 to the device-coherent level) and waits for them; lane 0 then
         // counts the workgroup in.  The last to count reads every part back
-        // (its own included), all of one part's loads in flight at once, and
-        // adds them in part order: the same bits whichever workgroup is last.
+        // (its own included) and adds them in part order: the same bits
+        // whichever workgroup is last.
         constexpr int kTot = RT * AT * 4 * 64;
         double *parts = a.ks_part + static_cast<size_t>(range) * ksplit * kTot;
 #pragma unroll
@@ -285,24 +317,12 @@ __device__ __forceinline__ void f64_body(const F64Args &a) {
         if (lane == 0) done = __hip_atomic_fetch_add(a.ks_count + range, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         done = __builtin_amdgcn_readfirstlane(done);
         if (done != static_cast<uint32_t>(ksplit - 1)) return;
-        for (int s2 = 0; s2 < ksplit; ++s2) {
-            double p[RT][AT][4];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int t = 0; t < AT; ++t)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        p[rt][t][v] = __hip_atomic_load(
-                            parts + static_cast<size_t>(s2) * kTot + ((rt * AT + t) * 4 + v) * 64 + lane,
-                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int t = 0; t < AT; ++t)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[rt][t][v] = s2 == 0 ? p[rt][t][v] : acc[rt][t][v] + p[rt][t][v];
-        }
+        if (ksplit == 2)
+            combine_parts<2, RT, AT>(parts, lane, acc);
+        else if (ksplit == 4)
+            combine_parts<4, RT, AT>(parts, lane, acc);
+        else
+            combine_parts<8, RT, AT>(parts, lane, acc);
         if (lane == 0) __hip_atomic_store(a.ks_count + range, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (row >= a.n) return;
