@@ -20,10 +20,12 @@
 // Work split: one workgroup per one or two 16-row weight tiles.  Its 8 waves
 // take the blocks of k in turn (wave g: blocks g, g + 8, ...) for every weight
 // and activation tile, so each weight block is read by one wave of one
-// workgroup; the waves' partial sums are added in wave order at the end.  Operands come from
-// memory with range-checked buffer loads, a chunk of D blocks ahead of the
-// MFMAs.  Every workgroup reads the stack (through L2); HBM serves each weight
-// block one time.
+// workgroup; the waves' partial sums are added in wave order at the end.
+// Operands come from memory with range-checked buffer loads, a chunk of D
+// blocks ahead of the MFMAs.  Every workgroup reads the stack (through L2); HBM
+// serves each weight block one time.  With a caller workspace (the K split,
+// f64_mma_split_kernel) a workgroup takes two tiles and a 2nd, 4th or 8th of
+// k, and the parts of a tile pair are added across workgroups at the end.
 #include <algorithm>
 
 #include "device.h"
