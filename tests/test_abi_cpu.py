@@ -234,12 +234,32 @@ def test_split_projection_validation():
     assert _mws(work=BASE + 100 * MB) == ALIAS                    # inside the weights
     assert _mws(work=BASE + 130 * MB + 4096) == ALIAS             # inside the scales
     assert _mws(residual=BASE + 132 * MB + 4096) == ALIAS         # residual inside the workspace
+    # empty problems enqueue nothing and need no workspace
+    assert _mws(n=0, work=None) == OK
+    assert _mws(rows=0, work=None) == OK
     # the projection's own checks come first
     assert _mws(mode=5) == MODE
     assert _mws(k=100) == SHAPE
     assert _mws(hi=None) == NULL
     assert _mws(y=BASE + 131 * MB + 2) == ALIGN
     assert _mws(y=BASE + 128 * MB + 4096) == ALIAS                # y over hi
+
+
+def test_split_projection_validation_f32():
+    """The f32 mode through the workspace entry (4096 x 8192, 16 rows: weights
+    from BASE, x 512 KiB at +64 MiB, y at +66 MiB, the workspace at +68 MiB)."""
+    lib = q8.lib()
+    need = lib.q8_matmul_rows_workspace_bytes(0, 4096, 8192, 16)
+    assert need > 0
+
+    def f(x=BASE + 64 * MB, y=BASE + 66 * MB, work=BASE + 68 * MB, work_bytes=need):
+        return lib.q8_matmul_rows_ws(0, BASE, 4096, 8192, 16, None, None, None, x, None, y, work, work_bytes, None)
+
+    assert f(work=None) == NULL
+    assert f(work_bytes=need - 8) == SHAPE
+    assert f(x=BASE + 64 * MB + 4) == ALIGN
+    assert f(work=BASE + 64 * MB + 128 * 1024) == ALIAS               # over x
+    assert f(work=BASE + 66 * MB + 64) == ALIAS                       # over y
 
 
 def test_argmax_workspace_size():
