@@ -274,3 +274,34 @@ def test_split_misaligned_weights_run_unsplit():
     assert bool((ws == 3).all())
     r, a = _expected(mode, blocks, n, k, x, None)
     gate(y.cpu().numpy(), r, a, "k split, misaligned weights")
+
+
+def test_split_calls_queued_back_to_back():
+    """48 split calls of varying shapes and modes queued on one stream, sharing
+    one workspace, with no host synchronization between them: every output
+    equals the same call run alone (the counters each call leaves at zero are
+    what the next one starts from)."""
+    shapes = [(4096, 14336, 16, "i8x2"), (2048, 14336, 5, "i8"), (1000, 8192, 33, "f32"),
+              (4096, 14336, 64, "i8"), (512, 131072, 2, "i8x2"), (4096, 8192, 24, "f32")]
+    cases = []
+    for i, (n, k, rows, mode) in enumerate(shapes):
+        assert q8.matmul_rows_workspace_bytes(mode, n, k, rows) > 0, (n, k, rows, mode)
+        blocks, x, _ = _case(n, k, rows, mode, False, seed=2200 + i)
+        cases.append((n, k, rows, mode, _dev(blocks), _stack(mode, _dev(x))))
+    big = max(q8.matmul_rows_workspace_bytes(m, n, k, r) for n, k, r, m in shapes)
+    shared = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    say("k split, 48 calls queued")
+    order = [i % len(cases) for i in range(48)]
+    outs = []
+    for i in order:
+        n, k, rows, mode, w, act = cases[i]
+        outs.append(q8.matmul_rows_ws(mode, w, n, k, workspace=shared, **act))
+    torch.cuda.synchronize()
+    assert _counters_zero(shared, 0)
+    for i, (n, k, rows, mode, w, act) in enumerate(cases):
+        fresh = torch.zeros(q8.matmul_rows_workspace_bytes(mode, n, k, rows), dtype=torch.uint8, device="cuda")
+        ref = q8.matmul_rows_ws(mode, w, n, k, workspace=fresh, **act)
+        torch.cuda.synchronize()
+        for j, o in zip(order, outs):
+            if j == i:
+                assert torch.equal(o, ref), (n, k, rows, mode)
