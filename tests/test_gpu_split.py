@@ -305,3 +305,40 @@ def test_split_calls_queued_back_to_back():
         for j, o in zip(order, outs):
             if j == i:
                 assert torch.equal(o, ref), (n, k, rows, mode)
+
+
+def _random_split_shapes(count, seed):
+    """Seeded (n, k, rows, mode, residual) draws, kept to those the library
+    splits, every stack under 4096 x 14336 x 24 multiply-adds."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    while len(out) < count:
+        mode = rng.choice(["i8", "i8x2", "f32"])
+        n = rng.choice([rng.randint(1, 4096), rng.randint(1, 1024), rng.randint(3000, 4096)])
+        k = 256 * rng.randint(4, 112) if mode != "f32" else 64 * rng.randint(8, 400)
+        rows = rng.randint(2, 70)
+        if n * k * rows > 4096 * 14336 * 24 or q8.matmul_rows_workspace_bytes(mode, n, k, rows) == 0:
+            continue
+        out.append((n, k, rows, mode, rng.random() < 0.5))
+    return out
+
+
+def test_split_random_shapes():
+    """Sixteen seeded random shapes that split (all three modes, ragged n and
+    k, 2..70 rows): the gate against the oracle, the same bits twice, counters
+    back at zero."""
+    for i, (n, k, rows, mode, with_res) in enumerate(_random_split_shapes(16, seed=12345)):
+        say("k split random", i, n, k, rows, mode, with_res)
+        blocks, x, res = _case(n, k, rows, mode, with_res, seed=3000 + i)
+        w = _dev(blocks)
+        act = _stack(mode, _dev(x))
+        resd = None if res is None else _dev(res)
+        ws = torch.zeros(q8.matmul_rows_workspace_bytes(mode, n, k, rows), dtype=torch.uint8, device="cuda")
+        y = q8.matmul_rows_ws(mode, w, n, k, residual=resd, workspace=ws, **act)
+        y2 = q8.matmul_rows_ws(mode, w, n, k, residual=resd, workspace=ws, **act)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2)
+        assert _counters_zero(ws, n)
+        r, a = _expected(mode, blocks, n, k, x, res)
+        gate(y.cpu().numpy(), r, a, f"k split random {n}x{k} rows={rows} {mode}")
