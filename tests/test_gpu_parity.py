@@ -6,6 +6,8 @@ projection.  Quantized bytes and int32 block sums must match bit for bit; f32
 outputs must pass the gate of helpers.gate.  Every workload call is run at its
 full size.
 """
+import random
+
 import numpy as np
 import pytest
 import torch
@@ -223,6 +225,37 @@ def test_ragged_shapes(mode, n, k, rows):
     y, *_ = gpu_path(call, to_dev(blocks), x, res)
     (r, a), _ = oracle_path(call, blocks, x, res)
     gate(y, r, a, f"ragged {mode} {n}x{k} rows={rows}")
+
+
+def _random_shapes(count, seed):
+    """Seeded (n, k, rows, mode) draws over every dispatch path: k any multiple
+    of 64 (the GEMV where it is not a multiple of 256), 1..70 rows, n from 1
+    to 20000, each stack under 4096 x 14336 x 16 multiply-adds."""
+    rng = random.Random(seed)
+    out = []
+    while len(out) < count:
+        mode = rng.choice(["f32", "i8", "i8x2"])
+        n = rng.choice([rng.randint(1, 300), rng.randint(300, 5000), rng.randint(5000, 20000)])
+        k = 64 * rng.randint(1, 160)
+        rows = rng.choice([rng.randint(1, 8), rng.randint(9, 70)])
+        if n * k * rows <= 4096 * 14336 * 16:
+            out.append((n, k, rows, mode))
+    return out
+
+
+def test_random_shapes():
+    """24 seeded random shapes with outliers in weights and activations and a
+    residual, through q8_matmul_rows, against the oracle."""
+    for i, (n, k, rows, mode) in enumerate(_random_shapes(24, seed=777)):
+        say("random", i, mode, n, k, rows)
+        w = synth.weights(n, k, seed=7000 + i, outlier_frac=0.05)
+        x = synth.activations(rows, k, seed=7100 + i, outlier_frac=0.05)
+        res = synth.normal(7200 + i, (rows, n))
+        blocks = oracle.quantize_weights(w)
+        call = workloads.Call("random", n, k, rows, mode, "matmul_rows", w_seed=0)
+        y, *_ = gpu_path(call, to_dev(blocks), x, res)
+        (r, a), _ = oracle_path(call, blocks, x, res)
+        gate(y, r, a, f"random {mode} {n}x{k} rows={rows}")
 
 
 def test_stack_rows_equal_single_rows():
